@@ -1,0 +1,27 @@
+"""CPU oracle for the per-step batched sampler (float64, NumPy).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link anything here: only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` use it.  It shares no code with the HIP
+library under ``decode_step_token_amd/``.
+
+Pins (each in ``tests/test_oracle_pins.py``):
+
+* ``philox``: equals ``numpy.random.Philox`` (Philox-4x64-10) block outputs.
+* ``row_params``/``sample_row``: the pages' worked example (closed forms and
+  draw frequency), argmax identities, the full-softmax identity against
+  ``scipy.special.softmax``, exact rational top-p cut-offs, the top-k set
+  against ``heapq.nsmallest``, the draw against ``numpy.searchsorted`` and a
+  brute-force sweep of ``u``, the filter-order counterexample.
+* ``write_tokens``: NumPy fancy-index assignment.
+"""
+from .philox import philox4x64, request_uniform, request_word, uniform24
+from .sampler_ref import (CUT_BAND, DRAW_BAND, MIN_P, MIN_T, RowParams, RowResult,
+                          descending_order, filter_sorted, inverse_cdf, row_params,
+                          sample_batch, sample_row, widen_logits, write_tokens)
+
+__all__ = [
+    "philox4x64", "request_uniform", "request_word", "uniform24", "CUT_BAND", "DRAW_BAND",
+    "MIN_P", "MIN_T", "RowParams", "RowResult", "descending_order", "filter_sorted",
+    "inverse_cdf", "row_params", "sample_batch", "sample_row", "widen_logits", "write_tokens",
+]

@@ -1,0 +1,243 @@
+"""fp64 CPU oracle of the per-step batched sampler and the token write-back.
+
+TEST INFRASTRUCTURE.  This is the plain, slow, obviously-correct statement of
+what the sampler computes; it is never on the product path.  Only ``tests/``,
+``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg may import it.
+It shares no code with the HIP library and imports nothing from it.
+
+It follows the mini-sglang pages step by step, in float64:
+
+* "The engine and the sampler", section "The sampler" -- ``Sampler.prepare``
+  (clamps ``MIN_T = MIN_P = 1e-6``, ``top_k < 1`` means the whole vocabulary,
+  ``top_p`` clamped to [1e-6, 1], an all-greedy batch carries no temperature
+  array and is decided by argmax) and ``sample_torch`` (softmax of
+  logits / T, sort descending, top-k mask by rank, renormalise, mask the
+  ranks whose preceding mass is already >= top_p, scatter back to index
+  order, one categorical draw).  The same section states the order: top-k
+  first, then top-p, and that the most likely token is always kept.
+* "The engine and the sampler", section "forward_batch": tokens are int32;
+  one copy stays on the device, one goes to the host.
+* "The scheduler skeleton and the offline interface", section "Preparing a
+  batch" (``_make_write_tuple``) and ``_forward``: the token is written to
+  ``token_pool[row, col]``; a column of -1 lands in the last column.
+
+Readings taken where the pages leave a step open (each is listed in the
+design notes):
+
+* a row is greedy iff its temperature is not above float32(1e-6); greedy
+  rows take the exact argmax (lowest index on ties), not a tiny-T softmax;
+* NaN temperature -> greedy; NaN top_p -> 1e-6 (clamp order max then min);
+* the descending order ranks by the logit value with ties by ascending index
+  (softmax is strictly monotone for T > 0), and -0.0 equals +0.0;
+* ``top_k >= V`` is the same as disabled; ``top_p >= 1`` disables top-p;
+* the top-p test is strict: keep rank j iff the exclusive prefix of the
+  renormalised post-top-k masses is < top_p;
+* the categorical draw is an inverse CDF in ascending token index with a
+  strict ``>``: token = min{i : C_i > u}, ``u`` from the keyed Philox stream;
+* the final distribution is the kept masses divided by their sum.
+
+Ambiguity flags (decisions that rounding order may legitimately flip):
+``draw_ambiguous`` when ``u`` lies within 1e-5 of a CDF boundary, and
+``cutoff_ambiguous`` when an exclusive prefix lies within 1e-6 of top_p.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+
+from .philox import request_uniform, request_word
+
+MIN_T = float(np.float32(1e-6))
+MIN_P = float(np.float32(1e-6))
+DRAW_BAND = 1e-5
+CUT_BAND = 1e-6
+
+
+def widen_logits(logits: np.ndarray, dtype: str) -> np.ndarray:
+    """Logits as float64: bf16 bit patterns shifted into the top half of a
+    float32, or float32 values, both widened exactly."""
+    if dtype == "bf16":
+        f32 = (np.asarray(logits).astype(np.uint32) << np.uint32(16)).view(np.float32)
+        return f32.astype(np.float64)
+    return np.asarray(logits, dtype=np.float32).astype(np.float64)
+
+
+@dataclass
+class RowParams:
+    greedy: bool
+    T: float          # effective temperature (float32 value, widened)
+    k: int            # effective top-k (V when disabled)
+    p: float          # effective top-p (1.0 when disabled)
+
+
+def row_params(V: int, T: Optional[float], k: Optional[int], p: Optional[float]) -> RowParams:
+    """``Sampler.prepare``'s clamps for one request, evaluated in float32."""
+    if T is None:
+        return RowParams(True, MIN_T, 1, 1.0)
+    t32 = np.float32(T)
+    greedy = not (t32 > np.float32(MIN_T))
+    T_eff = float(t32) if not greedy else MIN_T
+    k_eff = V if (k is None or int(k) < 1 or int(k) >= V) else int(k)
+    if p is None:
+        p_eff = 1.0
+    else:
+        p32 = np.float32(p)
+        p_eff = float(p32) if p32 > np.float32(MIN_P) else MIN_P
+        p_eff = min(p_eff, 1.0)
+    return RowParams(greedy, T_eff, k_eff, p_eff)
+
+
+def descending_order(x: np.ndarray) -> np.ndarray:
+    """Ranks by value descending, ties by ascending index (stable sort of -x)."""
+    return np.argsort(-x, kind="stable")
+
+
+def filter_sorted(q_sorted: np.ndarray, k: int, p: float, order: str = "k_then_p") -> int:
+    """Length n of the kept prefix of descending-sorted probabilities.
+
+    ``k_then_p`` (the pages' order): zero the ranks >= k, renormalise, keep a
+    rank while the mass strictly before it is < p.  ``p_then_k`` applies the
+    same two masks in the opposite order (used only to show that the order
+    matters).
+    """
+    V = len(q_sorted)
+    k = min(k, V)
+    if order == "k_then_p":
+        if p >= 1.0:
+            return k
+        q = q_sorted[:k] / q_sorted[:k].sum()
+        before = np.concatenate(([0.0], np.cumsum(q)[:-1]))
+        return int(np.count_nonzero(before < p))
+    if order == "p_then_k":
+        n = V
+        if p < 1.0:
+            q = q_sorted / q_sorted.sum()
+            before = np.concatenate(([0.0], np.cumsum(q)[:-1]))
+            n = int(np.count_nonzero(before < p))
+        return min(n, k)
+    raise ValueError(order)
+
+
+def inverse_cdf(r: np.ndarray, u: float) -> int:
+    """min{i : sum_{j<=i} r_j > u} in ascending token index; if rounding
+    leaves the last partial sum <= u, the largest index with r_i > 0."""
+    c = np.cumsum(r)
+    hit = np.flatnonzero(c > u)
+    if hit.size:
+        return int(hit[0])
+    return int(np.flatnonzero(r > 0)[-1])
+
+
+@dataclass
+class RowResult:
+    token: int
+    greedy: bool
+    r: np.ndarray                 # final distribution over V (float64)
+    kept: int                     # length of the kept prefix of the descending order
+    order_prefix: np.ndarray      # descending-order indices of the first min(k_eff, 64) ranks
+    u: float
+    word0: int
+    params: RowParams
+    draw_ambiguous: bool = False
+    acceptable: List[int] = field(default_factory=list)
+    cutoff_ambiguous: bool = False
+    alt_r: Dict[int, np.ndarray] = field(default_factory=dict)   # kept count -> r
+    alt_acceptable: Dict[int, List[int]] = field(default_factory=dict)
+
+
+def _distribution(x: np.ndarray, T: float, pi: np.ndarray, n: int) -> np.ndarray:
+    m = x.max()
+    w = np.exp((x - m) / T)
+    prob = w / w.sum()
+    r = np.zeros_like(prob)
+    keep = pi[:n]
+    r[keep] = prob[keep]
+    return r / r.sum()
+
+
+def _acceptable(r: np.ndarray, u: float):
+    c = np.cumsum(r)
+    prev = np.concatenate(([0.0], c[:-1]))
+    kept = r > 0
+    ok = np.flatnonzero(kept & (prev - DRAW_BAND <= u) & (u < c + DRAW_BAND))
+    near = np.abs(np.concatenate((prev[kept], c[kept])) - u).min() < DRAW_BAND
+    return bool(near), [int(i) for i in ok]
+
+
+def sample_row(x: np.ndarray, params: RowParams, u: float, word0: int = 0,
+               order: str = "k_then_p", want_alternatives: bool = True) -> RowResult:
+    """One request: greedy argmax, or softmax -> top-k -> top-p -> draw."""
+    V = len(x)
+    if params.greedy:
+        tok = int(np.argmax(x))
+        r = np.zeros(V)
+        r[tok] = 1.0
+        return RowResult(tok, True, r, 1, np.array([tok]), u, word0, params)
+
+    pi = descending_order(x)
+    m = x.max()
+    w = np.exp((x - m) / params.T)          # softmax(logits / T), max subtracted
+    prob = w / w.sum()
+    q_sorted = prob[pi]
+    n = filter_sorted(q_sorted, params.k, params.p, order)
+    r = _distribution(x, params.T, pi, n)
+    tok = inverse_cdf(r, u)
+    res = RowResult(tok, False, r, n, pi[:min(params.k, 64)].copy(), u, word0, params)
+    res.draw_ambiguous, res.acceptable = _acceptable(r, u)
+
+    if order == "k_then_p" and params.p < 1.0 and want_alternatives:
+        k = min(params.k, V)
+        q = q_sorted[:k] / q_sorted[:k].sum()
+        before = np.concatenate(([0.0], np.cumsum(q)[:-1]))
+        if np.any(np.abs(before - params.p) < CUT_BAND):
+            res.cutoff_ambiguous = True
+            for n_alt in (n - 1, n + 1):
+                if 1 <= n_alt <= k:
+                    r_alt = _distribution(x, params.T, pi, n_alt)
+                    res.alt_r[n_alt] = r_alt
+                    res.alt_acceptable[n_alt] = _acceptable(r_alt, u)[1] + [inverse_cdf(r_alt, u)]
+    return res
+
+
+def _opt(a: Optional[np.ndarray], b: int):
+    return None if a is None else a[b]
+
+
+def sample_batch(logits: np.ndarray, dtype: str, temperature: Optional[np.ndarray],
+                 top_k: Optional[np.ndarray], top_p: Optional[np.ndarray],
+                 uid: np.ndarray, step: int, seed: int, rows=None,
+                 order: str = "k_then_p") -> List[RowResult]:
+    """Every request of one decode step (or the subset ``rows``)."""
+    X = widen_logits(logits, dtype)
+    B, V = X.shape
+    out = []
+    for b in (range(B) if rows is None else rows):
+        prm = row_params(V, _opt(temperature, b), _opt(top_k, b), _opt(top_p, b))
+        if temperature is None:
+            u, w0 = 0.0, 0
+        else:
+            w0 = request_word(seed, int(uid[b]), step)
+            u = request_uniform(seed, int(uid[b]), step)
+        out.append(sample_row(X[b], prm, u, w0, order))
+    return out
+
+
+def write_tokens(pool: np.ndarray, rows: np.ndarray, cols: np.ndarray, tokens: np.ndarray):
+    """``token_pool[rows, cols] = tokens`` with column -1 meaning the last
+    column; an out-of-range (row, col) is skipped and reported.
+
+    Returns (new pool, host copy of the tokens, out_of_range flag)."""
+    out = pool.copy()
+    R, C = out.shape
+    bad = False
+    for b in range(len(tokens)):
+        r, c = int(rows[b]), int(cols[b])
+        if c == -1:
+            c = C - 1
+        if 0 <= r < R and 0 <= c < C:
+            out[r, c] = np.int32(tokens[b])
+        else:
+            bad = True
+    return out, np.asarray(tokens, dtype=np.int32).copy(), bad

@@ -1,0 +1,344 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test checks the oracle against a value the pages print, a closed form,
+a library routine with a documented tie rule, exact dyadic arithmetic, or a
+brute-force sweep.  None of these re-types the oracle's own formula.
+"""
+import heapq
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+
+import oracle
+from oracle import (filter_sorted, inverse_cdf, philox4x64, request_uniform, request_word,
+                    row_params, sample_batch, sample_row, widen_logits, write_tokens)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+M64 = (1 << 64) - 1
+
+
+# ---------------------------------------------------------------- Philox --
+
+def _numpy_block(counter, key):
+    """First block of numpy.random.Philox (Philox-4x64-10) for `counter`.
+
+    NumPy increments its 256-bit counter before producing a block, so the
+    generator is started one below the counter we want."""
+    c = sum(int(w) << (64 * i) for i, w in enumerate(counter))
+    c = (c - 1) % (1 << 256)
+    words = np.array([(c >> (64 * i)) & M64 for i in range(4)], dtype=np.uint64)
+    bg = np.random.Philox(counter=words, key=np.array(key, dtype=np.uint64))
+    return tuple(int(v) for v in bg.random_raw(4))
+
+
+@pytest.mark.parametrize("counter,key", [
+    ((0, 0, 0, 0), (0, 0)),
+    ((1, 0, 0, 0), (42, 0)),
+    ((0, 1, 0, 0), (42, 0)),          # borrow across words when starting NumPy one below
+    ((7, 1999, 0, 0), (42, 0)),
+    ((M64, M64, M64, M64), (M64, M64)),
+    ((0x243F6A8885A308D3, 0x13198A2E03707344, 0xA4093822299F31D0, 0x082EFA98EC4E6C89),
+     (0x452821E638D01377, 0xBE5466CF34E90C6C)),
+])
+def test_philox_matches_numpy(counter, key):
+    assert philox4x64(counter, key) == _numpy_block(counter, key)
+
+
+def test_request_word_keys_and_twos_complement():
+    # uid -1 is the all-ones counter word (the engine's dummy request has uid -1)
+    assert request_word(42, -1, 3) == _numpy_block((M64, 3, 0, 0), (42, 0))[0]
+    assert request_word(42, 5, 9) == _numpy_block((5, 9, 0, 0), (42, 0))[0]
+    assert request_word(7, 5, 9) != request_word(42, 5, 9)
+
+
+def test_uniform_is_24bit_dyadic_and_uniform():
+    us = np.array([request_uniform(42, uid, 0) for uid in range(20000)])
+    assert np.all(us >= 0.0) and np.all(us < 1.0)
+    assert np.all(us * 2 ** 24 == np.floor(us * 2 ** 24))
+    assert scipy.stats.kstest(us, "uniform").pvalue > 1e-3
+
+
+# -------------------------------------------------- the pages' example --
+
+def _golden():
+    with open(os.path.join(GOLDEN, "pages_worked_example.json")) as f:
+        return json.load(f)
+
+
+def test_pages_example_supports_and_closed_form():
+    g = _golden()
+    x = np.array(g["logits"], dtype=np.float64)
+    V = g["vocab_size"]
+    for req in g["requests"]:
+        prm = row_params(V, req["temperature"], req["top_k"], req["top_p"])
+        res = sample_row(x, prm, 0.5)
+        assert sorted(np.flatnonzero(res.r > 0).tolist()) == req["support"]
+        for u in np.linspace(0, 1 - 2 ** -24, 257):
+            assert sample_row(x, prm, float(u)).token in req["support"]
+    # request 0: top-k 2 renormalises to e^5/(e^5+e^4) and e^4/(e^5+e^4)
+    prm = row_params(V, 1.0, 2, 1.0)
+    r = sample_row(x, prm, 0.0).r
+    e = math.e
+    np.testing.assert_allclose(r, [e / (1 + e), 1 / (1 + e), 0, 0, 0, 0], rtol=0, atol=1e-15)
+
+
+def test_pages_example_all_greedy_batch():
+    g = _golden()
+    assert g["all_greedy_batch_has_no_temperature"]
+    x = np.array([g["logits"]] * 2, dtype=np.float32)
+    res = sample_batch(x, "f32", None, None, None, np.arange(2), 0, 42)
+    assert [r.token for r in res] == [0, 0] and all(r.greedy for r in res)
+
+
+def test_pages_example_draw_frequency():
+    g = _golden()
+    x = np.array(g["logits"], dtype=np.float64)
+    prm = row_params(g["vocab_size"], 1.0, 2, 1.0)
+    toks = [sample_row(x, prm, request_uniform(42, 0, s)).token for s in range(g["draws"])]
+    f0 = toks.count(0) / len(toks)
+    assert abs(f0 - g["freq_token0_request0"]) < g["freq_tolerance"]
+    assert set(toks) == {0, 1}
+
+
+# ------------------------------------------------------ argmax identities --
+
+def _rows_with_ties(rng, n, V):
+    X = rng.normal(0, 2, (n, V))
+    for b in range(0, n, 2):          # every other row: the maximum appears twice
+        X[b, int(rng.integers(0, V))] = X[b].max()
+    return X.astype(np.float32).astype(np.float64)
+
+
+def test_greedy_is_numpy_first_argmax():
+    rng = np.random.default_rng(1)
+    X = _rows_with_ties(rng, 40, 300)
+    X[3, :] = 1.25  # all equal: index 0
+    for x in X:
+        for T in (None, 0.0, 1e-6, float(np.float32(1e-6)), -3.0, float("nan")):
+            prm = row_params(len(x), T, 50, 0.9)
+            assert prm.greedy
+            assert sample_row(x, prm, 0.3).token == int(np.argmax(x))
+
+
+def test_topk1_is_argmax_for_every_u():
+    rng = np.random.default_rng(2)
+    X = _rows_with_ties(rng, 20, 200)
+    for x in X:
+        prm = row_params(len(x), float(rng.uniform(0.2, 2)), 1, float(rng.uniform(0.1, 1)))
+        for u in (0.0, 2 ** -24, 0.5, 1 - 2 ** -24):
+            assert sample_row(x, prm, u).token == int(np.argmax(x))
+
+
+def test_tiny_temperature_gives_argmax():
+    """A temperature just above the greedy cut (1e-4) through the sampling
+    path collapses to the argmax on rows whose maximum is unique."""
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        x = rng.normal(0, 2, 500)
+        top = np.argsort(-x)
+        x[top[0]] = x[top[1]] + 0.05
+        prm = row_params(500, 1e-4, -1, 1.0)
+        assert not prm.greedy
+        for u in (1e-12, 0.25, 0.5, 1 - 2 ** -24):
+            assert sample_row(x, prm, u).token == int(top[0])
+
+
+# ------------------------------------------------ softmax identities ----
+
+def test_full_softmax_matches_scipy():
+    rng = np.random.default_rng(4)
+    for T in (0.3, 0.7, 1.0, 1.5, 3.0):
+        x = rng.normal(0, 3, 2000)
+        prm = row_params(2000, T, -1, 1.0)
+        r = sample_row(x, prm, 0.5).r
+        want = scipy.special.softmax(x / float(np.float32(T)))
+        np.testing.assert_allclose(r, want, rtol=1e-12, atol=1e-15)
+
+
+def test_two_token_closed_form():
+    for a, b, T in ((1.0, 0.0, 0.5), (2.0, 3.5, 1.5), (-1.0, -1.25, 0.3)):
+        prm = row_params(2, T, -1, 1.0)
+        r = sample_row(np.array([a, b]), prm, 0.5).r
+        t = float(np.float32(T))
+        assert abs(r[0] - 1.0 / (1.0 + math.exp((b - a) / t))) < 1e-15
+
+
+# ---------------------------------------------------------- top-k set ---
+
+def test_topk_set_matches_heapq_with_index_ties():
+    rng = np.random.default_rng(5)
+    for trial in range(30):
+        V = int(rng.integers(2, 400))
+        x = np.round(rng.normal(0, 1.5, V), 1)          # many exact ties
+        if trial % 5 == 0:
+            x[: V // 2] = 0.0
+            x[V // 2] = -0.0
+        k = int(rng.integers(1, V + 1))
+        prm = row_params(V, 0.9, k, 1.0)
+        res = sample_row(x, prm, 0.5)
+        want = heapq.nsmallest(min(k, V), range(V), key=lambda i: (-x[i] + 0.0, i))
+        assert res.kept == min(k, V)
+        assert res.order_prefix.tolist() == want[:min(k, 64)]
+        assert sorted(np.flatnonzero(res.r > 0)) == sorted(want)
+
+
+def test_bf16_rows_widen_exactly():
+    bits = np.array([[0x3F80, 0xC000, 0x8000, 0x0000, 0x4049, 0x7F7F]], dtype=np.uint16)
+    x = widen_logits(bits, "bf16")[0]
+    assert x[0] == 1.0 and x[1] == -2.0 and x[2] == 0.0 and math.copysign(1, x[2]) == -1
+    assert x[4] == 3.140625 and x[5] == float(np.float32(3.3895313892515355e38))
+
+
+# --------------------------------------------------- top-p, exact cases --
+
+@pytest.mark.parametrize("q,k,p,n", [
+    # exclusive prefixes 0, 1/2, 3/4, 7/8; strict "<" drops rank 2 at p = 3/4
+    ((0.5, 0.25, 0.125, 0.125), 4, 0.75, 2),
+    ((0.5, 0.25, 0.125, 0.125), 4, 0.75 + 2 ** -20, 3),
+    ((0.5, 0.25, 0.125, 0.125), 4, 0.5, 1),
+    ((0.5, 0.25, 0.125, 0.125), 4, 2 ** -30, 1),        # the most likely token is always kept
+    ((0.5, 0.25, 0.125, 0.125), 4, 1.0, 4),
+    # top-k 2 renormalises (1/2, 1/4) to (2/3, 1/3): prefix 2/3 >= 0.6 drops rank 1
+    ((0.5, 0.25, 0.125, 0.125), 2, 0.6, 1),
+    ((0.5, 0.25, 0.125, 0.125), 2, 0.6875, 2),
+    # the order example: (0.4, 0.3, 0.2, 0.1), k=3, p=0.42
+    ((0.4, 0.3, 0.2, 0.1), 3, 0.42, 1),
+])
+def test_top_p_cutoffs_exact(q, k, p, n):
+    assert filter_sorted(np.array(q), k, p) == n
+
+
+def test_filter_order_matters():
+    q = np.array([0.4, 0.3, 0.2, 0.1])
+    assert filter_sorted(q, 3, 0.42, "k_then_p") == 1
+    assert filter_sorted(q, 3, 0.42, "p_then_k") == 2
+
+
+def test_filter_order_brute_force():
+    """On every small grid case, top-k-then-top-p keeps a prefix no longer than
+    the reverse order, both are prefixes of the descending order, the kept
+    prefix is the shortest one whose renormalised mass reaches p, and some
+    cases differ."""
+    grid = [0.0, 0.5, 1.0, 2.0]
+    differ = 0
+    for V in (3, 4, 5):
+        for xs in itertools.product(grid, repeat=V):
+            x = np.array(xs)
+            if len(set(xs)) == 1:
+                continue
+            pi = np.argsort(-x, kind="stable")
+            for k in range(1, V + 1):
+                for p in (0.05, 0.25, 0.45, 0.65, 0.85, 0.95):
+                    prm = row_params(V, 1.0, k, p)
+                    a = sample_row(x, prm, 0.5, want_alternatives=False)
+                    b = sample_row(x, prm, 0.5, order="p_then_k", want_alternatives=False)
+                    assert a.kept <= b.kept
+                    assert set(np.flatnonzero(a.r > 0)) == set(pi[:a.kept].tolist())
+                    w = np.exp(x - x.max())[pi][:k]
+                    w = w / w.sum()
+                    assert w[:a.kept - 1].sum() < p
+                    assert a.kept == k or w[:a.kept].sum() >= p
+                    differ += a.kept != b.kept
+    assert differ > 0
+
+
+# ------------------------------------------------------------- the draw --
+
+def test_draw_matches_searchsorted():
+    rng = np.random.default_rng(6)
+    for _ in range(200):
+        V = int(rng.integers(1, 300))
+        x = rng.normal(0, 2, V)
+        prm = row_params(V, float(rng.uniform(0.3, 2)), int(rng.integers(-1, V + 2)),
+                         float(rng.uniform(0.05, 1.2)))
+        u = float(rng.integers(0, 1 << 24)) * 2 ** -24
+        res = sample_row(x, prm, u)
+        c = np.cumsum(res.r)
+        if c[-1] > u:
+            assert res.token == int(np.searchsorted(c, u, side="right"))
+        assert res.r[res.token] > 0
+
+
+def test_draw_measure_brute_force():
+    """Sweeping u over a 2^-16 grid, token i is drawn for a measure r_i."""
+    x = np.array([1.0, -0.5, 2.0, 0.25, 2.0])
+    prm = row_params(5, 0.8, 4, 0.97)
+    base = sample_row(x, prm, 0.0)
+    counts = np.zeros(5)
+    n = 1 << 16
+    for j in range(n):
+        counts[inverse_cdf(base.r, j / n)] += 1
+    np.testing.assert_allclose(counts / n, base.r, atol=1.0 / n)
+    # dyadic masses put every CDF boundary on the grid: token i owns exactly the
+    # half-open interval [C_{i-1}, C_i), i.e. r_i * n grid points
+    r = np.array([0.5, 0.0, 0.25, 0.125, 0.125])
+    counts = np.zeros(5)
+    for j in range(n):
+        counts[inverse_cdf(r, j / n)] += 1
+    assert np.array_equal(counts, r * n)
+    assert inverse_cdf(r, 0.5) == 2 and inverse_cdf(r, 0.0) == 0
+
+
+def test_batch_permutation_and_resume():
+    """Tokens follow (seed, uid, step), not the row position."""
+    rng = np.random.default_rng(7)
+    B, V = 12, 256
+    X = rng.normal(0, 2, (B, V)).astype(np.float32)
+    T = rng.uniform(0.3, 1.5, B).astype(np.float32)
+    k = rng.choice([-1, 5, 50], B).astype(np.int32)
+    p = rng.choice([1.0, 0.9], B).astype(np.float32)
+    uid = rng.integers(0, 10 ** 9, B)
+    a = [r.token for r in sample_batch(X, "f32", T, k, p, uid, 17, 42)]
+    perm = rng.permutation(B)
+    b = [r.token for r in sample_batch(X[perm], "f32", T[perm], k[perm], p[perm], uid[perm], 17, 42)]
+    assert [a[i] for i in perm] == b
+    c = [r.token for r in sample_batch(X, "f32", T, k, p, uid, 17, 42)]
+    assert a == c
+
+
+# ----------------------------------------------------------- prepare ----
+
+def test_prepare_clamps():
+    V = 100
+    assert row_params(V, 0.0, 5, 0.5).greedy
+    assert row_params(V, float(np.float32(1e-6)), 5, 0.5).greedy
+    assert not row_params(V, 1.1e-6, 5, 0.5).greedy
+    assert row_params(V, 0.7, 0, 1.0).k == V
+    assert row_params(V, 0.7, -1, 1.0).k == V
+    assert row_params(V, 0.7, V, 1.0).k == V
+    assert row_params(V, 0.7, V + 3, 1.0).k == V
+    assert row_params(V, 0.7, V - 1, 1.0).k == V - 1
+    assert row_params(V, 0.7, 5, 0.0).p == float(np.float32(1e-6))
+    assert row_params(V, 0.7, 5, 2.0).p == 1.0
+    assert row_params(V, 0.7, 5, float("nan")).p == float(np.float32(1e-6))
+    assert row_params(V, float("nan"), 5, 0.5).greedy
+
+
+# ------------------------------------------------------- write-back -----
+
+def test_write_tokens_matches_fancy_index():
+    rng = np.random.default_rng(8)
+    R, C, B = 16, 40, 10
+    pool = rng.integers(0, 1000, (R, C)).astype(np.int32)
+    rows = rng.permutation(R)[:B].astype(np.int64)
+    cols = rng.integers(-1, C, B).astype(np.int64)
+    cols[:2] = -1                      # "do not write": lands in the last column
+    toks = rng.integers(0, 1 << 20, B).astype(np.int32)
+    new, host, bad = write_tokens(pool, rows, cols, toks)
+    want = pool.copy()
+    want[rows, cols % C] = toks
+    assert np.array_equal(new, want) and np.array_equal(host, toks) and not bad
+    _, _, bad = write_tokens(pool, np.array([0, R]), np.array([0, 0]), np.array([1, 2]))
+    assert bad
+    _, _, bad = write_tokens(pool, np.array([0]), np.array([-2]), np.array([1]))
+    assert bad
+
+
+def test_module_header_marks_test_infrastructure():
+    assert "TEST INFRASTRUCTURE" in oracle.__doc__

@@ -1,0 +1,119 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check that a pin
+catches each one.  This guards the pins themselves: a pin that passes on a
+broken oracle would prove nothing."""
+import numpy as np
+import pytest
+
+import oracle.philox as ph
+import oracle.sampler_ref as sr
+from tests import test_oracle_pins as pins
+
+
+def _inclusive_prefix(q_sorted, k, p, order="k_then_p"):
+    k = min(k, len(q_sorted))
+    if p >= 1.0:
+        return k
+    q = q_sorted[:k] / q_sorted[:k].sum()
+    return int(np.count_nonzero(np.cumsum(q) < p))
+
+
+def _non_strict(q_sorted, k, p, order="k_then_p"):
+    k = min(k, len(q_sorted))
+    if p >= 1.0:
+        return k
+    q = q_sorted[:k] / q_sorted[:k].sum()
+    before = np.concatenate(([0.0], np.cumsum(q)[:-1]))
+    return int(np.count_nonzero(before <= p))
+
+
+def _no_renormalise(q_sorted, k, p, order="k_then_p"):
+    k = min(k, len(q_sorted))
+    if p >= 1.0:
+        return k
+    q = q_sorted[:k]
+    before = np.concatenate(([0.0], np.cumsum(q)[:-1]))
+    return int(np.count_nonzero(before < p))
+
+
+_real_filter = sr.filter_sorted
+
+
+def _p_then_k(q_sorted, k, p, order="k_then_p"):
+    return _real_filter(q_sorted, k, p, "p_then_k")
+
+
+def _distribution_times_T(x, T, pi, n):
+    return _real_distribution(x, 1.0 / T, pi, n)
+
+
+_real_distribution = sr._distribution
+_real_order = sr.descending_order
+
+
+def _last_index_ties(x):
+    # descending by value but ties by descending index
+    return np.lexsort((-np.arange(len(x)), -x))
+
+
+def _draw_ge(r, u):
+    c = np.cumsum(r)
+    hit = np.flatnonzero(c >= u)
+    return int(hit[0]) if hit.size else int(np.flatnonzero(r > 0)[-1])
+
+
+def _philox_no_key_bump(counter, key, rounds=10):
+    x0, x1, x2, x3 = (int(c) & ph.M64 for c in counter)
+    k0, k1 = (int(k) & ph.M64 for k in key)
+    for _ in range(rounds):
+        p0, p1 = ph.PHILOX_M0 * x0, ph.PHILOX_M1 * x2
+        x0, x1, x2, x3 = ((p1 >> 64) ^ x1 ^ k0, p1 & ph.M64, (p0 >> 64) ^ x3 ^ k1, p0 & ph.M64)
+    return (x0, x1, x2, x3)
+
+
+def _write_minus_one_to_first(pool, rows, cols, tokens):
+    return _real_write(pool, rows, np.where(np.asarray(cols) == -1, 0, cols), tokens)
+
+
+_real_write = sr.write_tokens
+
+
+def _run_pins(names):
+    for name in names:
+        fn = getattr(pins, name)
+        if name == "test_top_p_cutoffs_exact":
+            for args in [((0.5, 0.25, 0.125, 0.125), 4, 0.75, 2),
+                         ((0.5, 0.25, 0.125, 0.125), 2, 0.6, 1),
+                         ((0.4, 0.3, 0.2, 0.1), 3, 0.42, 1)]:
+                fn(*args)
+        elif name == "test_philox_matches_numpy":
+            fn((7, 1999, 0, 0), (42, 0))
+        else:
+            fn()
+
+
+PLANTS = [
+    ("filter_sorted", _inclusive_prefix, ["test_pages_example_supports_and_closed_form"]),
+    ("filter_sorted", _non_strict, ["test_top_p_cutoffs_exact"]),
+    ("filter_sorted", _no_renormalise, ["test_top_p_cutoffs_exact"]),
+    ("filter_sorted", _p_then_k, ["test_filter_order_brute_force"]),
+    ("_distribution", _distribution_times_T, ["test_two_token_closed_form"]),
+    ("descending_order", _last_index_ties, ["test_topk_set_matches_heapq_with_index_ties"]),
+    ("inverse_cdf", _draw_ge, ["test_draw_measure_brute_force"]),
+    ("write_tokens", _write_minus_one_to_first, ["test_write_tokens_matches_fancy_index"]),
+]
+
+
+@pytest.mark.parametrize("attr,bad,pin_names", PLANTS, ids=[p[1].__name__ for p in PLANTS])
+def test_planted_sampler_mistake_is_caught(monkeypatch, attr, bad, pin_names):
+    monkeypatch.setattr(sr, attr, bad)
+    for mod_name in ("filter_sorted", "inverse_cdf", "write_tokens"):
+        if attr == mod_name:
+            monkeypatch.setattr(pins, mod_name, bad)
+    with pytest.raises(Exception):    # a failed assertion, or the oracle breaking outright
+        _run_pins(pin_names)
+
+
+def test_planted_philox_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(pins, "philox4x64", _philox_no_key_bump)
+    with pytest.raises(AssertionError):
+        _run_pins(["test_philox_matches_numpy"])
