@@ -1,0 +1,201 @@
+"""Benchmark of the per-step batched sampler on one MI355X.
+
+One step = sample_batch (temperature -> top-k -> top-p -> draw for every
+request) + write_tokens (token-pool scatter, async copy to pinned host
+memory, completion ticket), on the workload the headline metric is quoted
+on: B=256 requests, V=151936, fp32 logits 2*Gumbel + a rank-4 term, per-request
+T ~ U[0.3, 1.5], top_k from {1, 20, 50, off}, top_p from {1, 0.95, 0.8}.
+The step counter advances every step (fresh Philox counters); as in the
+engine's overlapped loop, step s waits for the host copy of step s-1.
+
+Inputs are resident in HBM before timing.  The logits are copied into
+several distinct device buffers used in rotation, so that repeated reads of
+the same 155 MB cannot be served from the 256 MB Infinity Cache.
+
+Prints ONE JSON line (stdout).  Diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "sampled rows/sec and achieved HBM GB/s (% of peak) at B=256, V=151936"
+PARAM_BYTES_PER_ROW = 4 + 4 + 4 + 8 + 4   # T, top_k, top_p, uid read; token written
+WRITE_BYTES_PER_ROW = 8 + 8 + 4 + 4       # row, col, token read; pool cell written
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sources_digest() -> str:
+    csrc = os.path.join(ROOT, "decode_step_token_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """Counter-measured HBM bytes per launch from profiles/, if taken on the
+    current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            data = json.load(f)
+        rec = data.get(f"{kernel}@{workload}")
+        if rec and rec.get("sources_digest") == kernel_sources_digest():
+            return rec.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+    return None
+
+
+def cpu_baseline(w, seconds: float):
+    import oracle
+    t0 = time.perf_counter()
+    n = 0
+    for b in range(w.B):
+        oracle.sample_batch(w.logits, w.dtype, w.temperature, w.top_k, w.top_p, w.uid, w.step,
+                            w.seed, rows=[b])
+        n += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {w.B} rows of the same batch, fp64 NumPy oracle, one process"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--buffers", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this sampler runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(rows are independent: shard the batch, one process per GPU)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import decode_step_token_amd as dst
+    import workloads as wl
+
+    eprint("bench: generating the B=256 V=151936 fp32 workload")
+    w = wl.c3()
+    B, V = w.B, w.V
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    host_logits = torch.from_numpy(w.logits)
+    bufs = [host_logits.to(dev) for _ in range(args.buffers)]
+    T = torch.from_numpy(w.temperature).to(dev)
+    k = torch.from_numpy(w.top_k).to(dev)
+    p = torch.from_numpy(w.top_p).to(dev)
+    uid = torch.from_numpy(w.uid).to(dev)
+    pool = torch.from_numpy(w.pool.copy()).to(dev)
+    rows = torch.from_numpy(w.rows).to(dev)
+    cols0 = torch.from_numpy(w.cols).to(dev)
+    tokens = torch.empty(B, dtype=torch.int32, device=dev)
+    host_ring = [torch.empty(B, dtype=torch.int32).pin_memory() for _ in range(2)]
+    sampler = dst.Sampler(0, B, V, "f32", w.seed)
+    stream = torch.cuda.current_stream()
+
+    total = args.warmup + args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def step(s, timed_index=None):
+        if timed_index is not None:
+            starts[timed_index].record(stream)
+        sampler.sample(bufs[s % len(bufs)], temperature=T, top_k=k, top_p=p, uid=uid, step=s,
+                       tokens_out=tokens, stream=stream)
+        if timed_index is not None:
+            ends[timed_index].record(stream)
+        return sampler.write(pool, rows, cols0, tokens, host_ring[s % 2], stream)
+
+    eprint(f"bench: warmup {args.warmup} steps")
+    prev = None
+    for s in range(args.warmup):
+        t = step(s)
+        if prev is not None:
+            sampler.wait(prev)
+        prev = t
+    if prev is not None:
+        sampler.wait(prev)
+    torch.cuda.synchronize()
+
+    eprint(f"bench: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    prev = None
+    for i in range(args.steps):
+        t = step(args.warmup + i, i)
+        if prev is not None:
+            sampler.wait(prev)
+        prev = t
+    sampler.wait(prev)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    sampler.check()
+    sampler.close()
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    avg_kernel_ms = float(np.mean(kernel_ms))
+    alg_bytes = B * (V * 4 + PARAM_BYTES_PER_ROW)
+    achieved = alg_bytes / (avg_kernel_ms * 1e-3) / 1e9
+    eprint(f"bench: {ms_per_step * 1e3:.1f} us/step, sample_batch kernel avg "
+           f"{avg_kernel_ms * 1e3:.1f} us (p10 {np.percentile(kernel_ms, 10) * 1e3:.1f}, "
+           f"p90 {np.percentile(kernel_ms, 90) * 1e3:.1f}), {achieved:.0f} GB/s")
+
+    traffic = load_traffic("sample_batch", "c3")
+    cpu = None
+    if not args.no_cpu_baseline:
+        eprint(f"bench: timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": B / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "c3: B=256 V=151936 fp32 2*Gumbel+rank-4 logits, per-request "
+                               "T~U[0.3,1.5], top_k in {1,20,50,off}, top_p in {1,0.95,0.8}; "
+                               "token pool [256,4096]",
+                   "B": B, "V": V, "logits_dtype": "f32", "input_buffers": len(bufs),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "sample_batch", "kernel_avg_us": avg_kernel_ms * 1e3,
+                     "alg_bytes_per_launch": alg_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,238 @@
+"""ctypes binding of ``libdst_sampler.so`` (the C ABI in ``include/sampler.h``).
+
+Argument marshalling only: every step of the sampler runs in the HIP
+kernels.  PyTorch supplies device memory (``Tensor.data_ptr()``) and the
+stream (``torch.cuda.current_stream().cuda_stream``, a ``hipStream_t`` on
+ROCm).  The functions carry the C names; tensors are checked for device,
+dtype, shape and contiguity before their pointers cross the boundary.
+
+If the library has not been built, :func:`load` raises -- there is no
+fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libdst_sampler.so")
+
+SAMPLER_F32 = 0
+SAMPLER_BF16 = 1
+SAMPLER_DEBUG_TOPK = 64
+
+STATUS = {0: "SAMPLER_OK", -1: "SAMPLER_EINVAL", -2: "SAMPLER_ENOMEM", -3: "SAMPLER_EHIP",
+          -4: "SAMPLER_ENOTPINNED", -5: "SAMPLER_EDEVICE", -6: "SAMPLER_ETICKET"}
+
+EXPORTS = ("sampler_create", "sampler_destroy", "sample_batch", "write_tokens", "sampler_wait",
+           "sampler_query", "sampler_check", "sampler_strerror", "sampler_last_error")
+
+
+class SamplerError(RuntimeError):
+    def __init__(self, code: int, where: str, detail: str = ""):
+        self.code = code
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({detail})")
+
+
+class SamplerDebug(ctypes.Structure):
+    _fields_ = [("probs_out", ctypes.c_void_p), ("kept_out", ctypes.c_void_p),
+                ("topk_idx_out", ctypes.c_void_p), ("rand_out", ctypes.c_void_p)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"HIP sampler library not built: {path} (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, U64, INT = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                             ctypes.c_int)
+    lib.sampler_create.argtypes = [ctypes.POINTER(P), INT, I32, I32, I32, U64]
+    lib.sampler_destroy.argtypes = [P]
+    lib.sample_batch.argtypes = [P, P, P, I64, I32, P, P, P, P, U64, P, ctypes.POINTER(SamplerDebug)]
+    lib.write_tokens.argtypes = [P, P, P, I64, I64, P, P, P, I32, P, ctypes.POINTER(U64)]
+    lib.sampler_wait.argtypes = [P, U64]
+    lib.sampler_query.argtypes = [P, U64]
+    lib.sampler_check.argtypes = [P]
+    lib.sampler_strerror.argtypes = [INT]
+    lib.sampler_strerror.restype = ctypes.c_char_p
+    lib.sampler_last_error.argtypes = [P]
+    lib.sampler_last_error.restype = ctypes.c_char_p
+    for name in ("sampler_create", "sampler_destroy", "sample_batch", "write_tokens",
+                 "sampler_wait", "sampler_query", "sampler_check"):
+        getattr(lib, name).restype = INT
+    _lib = lib
+    return lib
+
+
+def _check(code: int, where: str, handle=None) -> int:
+    if code < 0:
+        detail = ""
+        if handle is not None:
+            detail = (load().sampler_last_error(handle) or b"").decode()
+        raise SamplerError(code, where, detail)
+    return code
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, n: Optional[int], device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if n is not None and t.numel() != n:
+        raise ValueError(f"{name}: expected {n} elements, got {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def sampler_create(device: int, max_batch: int, vocab_size: int, dtype: str = "f32",
+                   seed: int = 42) -> ctypes.c_void_p:
+    lib = load()
+    h = ctypes.c_void_p()
+    code = lib.sampler_create(ctypes.byref(h), int(device), int(max_batch), int(vocab_size),
+                              SAMPLER_F32 if dtype == "f32" else SAMPLER_BF16,
+                              int(seed) & ((1 << 64) - 1))
+    _check(code, "sampler_create")
+    return h
+
+
+def sampler_destroy(handle) -> None:
+    if handle:
+        _check(load().sampler_destroy(handle), "sampler_destroy")
+
+
+def sample_batch(handle, logits: torch.Tensor, temperature=None, top_k=None, top_p=None,
+                 uid=None, step: int = 0, tokens_out: Optional[torch.Tensor] = None,
+                 stream=None, debug: Optional[dict] = None, row_stride: Optional[int] = None,
+                 B: Optional[int] = None) -> torch.Tensor:
+    """``logits``: [B, >=V] float32 or bf16 tensor (bf16 may also be passed as
+    int16/uint16 bit patterns); returns (or fills) ``tokens_out`` int32 [B]."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D [B, V]")
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    dev = logits.device
+    B = logits.shape[0] if B is None else int(B)
+    stride = logits.stride(0) if row_stride is None else int(row_stride)
+    if tokens_out is None:
+        tokens_out = torch.empty(B, dtype=torch.int32, device=dev)
+    dbg = None
+    if debug:
+        dbg = SamplerDebug()
+        for field, dt in (("probs_out", torch.float32), ("kept_out", torch.int32),
+                          ("topk_idx_out", torch.int32), ("rand_out", torch.int64)):
+            t = debug.get(field)
+            setattr(dbg, field, None if t is None else _ptr(t, field, dt, None, dev).value)
+    code = load().sample_batch(
+        handle, _stream(stream), ctypes.c_void_p(logits.data_ptr()), stride, B,
+        _ptr(temperature, "temperature", torch.float32, B, dev),
+        _ptr(top_k, "top_k", torch.int32, B, dev),
+        _ptr(top_p, "top_p", torch.float32, B, dev),
+        _ptr(uid, "uid", torch.int64, B, dev),
+        int(step) & ((1 << 64) - 1),
+        _ptr(tokens_out, "tokens_out", torch.int32, None, dev),
+        ctypes.byref(dbg) if dbg is not None else None)
+    _check(code, "sample_batch", handle)
+    return tokens_out
+
+
+def write_tokens(handle, token_pool: torch.Tensor, rows: torch.Tensor, cols: torch.Tensor,
+                 tokens: torch.Tensor, host_out: Optional[torch.Tensor] = None,
+                 stream=None) -> int:
+    """``token_pool[rows, cols] = tokens`` on the device, async copy of
+    ``tokens`` into the pinned ``host_out``; returns the completion ticket."""
+    if token_pool.dim() != 2 or not token_pool.is_contiguous():
+        raise ValueError("token_pool must be a contiguous [R, C] tensor")
+    dev = token_pool.device
+    B = tokens.numel()
+    if host_out is not None:
+        if host_out.device.type != "cpu" or host_out.dtype != torch.int32 or host_out.numel() < B:
+            raise ValueError("host_out must be a cpu int32 tensor with >= B elements")
+    ticket = ctypes.c_uint64(0)
+    code = load().write_tokens(
+        handle, _stream(stream), _ptr(token_pool, "token_pool", torch.int32, None, dev),
+        token_pool.shape[0], token_pool.shape[1],
+        _ptr(rows, "rows", torch.int64, B, dev), _ptr(cols, "cols", torch.int64, B, dev),
+        _ptr(tokens, "tokens", torch.int32, B, dev), B,
+        None if host_out is None else ctypes.c_void_p(host_out.data_ptr()),
+        ctypes.byref(ticket))
+    _check(code, "write_tokens", handle)
+    return ticket.value
+
+
+def sampler_wait(handle, ticket: int) -> None:
+    _check(load().sampler_wait(handle, int(ticket)), "sampler_wait", handle)
+
+
+def sampler_query(handle, ticket: int) -> bool:
+    return bool(_check(load().sampler_query(handle, int(ticket)), "sampler_query", handle))
+
+
+def sampler_check(handle) -> None:
+    _check(load().sampler_check(handle), "sampler_check", handle)
+
+
+def sampler_strerror(code: int) -> str:
+    return load().sampler_strerror(int(code)).decode()
+
+
+class Sampler:
+    """Owning wrapper of one handle (one per engine and stream)."""
+
+    def __init__(self, device: int, max_batch: int, vocab_size: int, dtype: str = "f32",
+                 seed: int = 42):
+        self.vocab_size = vocab_size
+        self.dtype = dtype
+        self.handle = sampler_create(device, max_batch, vocab_size, dtype, seed)
+
+    def sample(self, logits, **kw) -> torch.Tensor:
+        return sample_batch(self.handle, logits, **kw)
+
+    def write(self, token_pool, rows, cols, tokens, host_out=None, stream=None) -> int:
+        return write_tokens(self.handle, token_pool, rows, cols, tokens, host_out, stream)
+
+    def wait(self, ticket: int) -> None:
+        sampler_wait(self.handle, ticket)
+
+    def query(self, ticket: int) -> bool:
+        return sampler_query(self.handle, ticket)
+
+    def check(self) -> None:
+        sampler_check(self.handle)
+
+    def close(self) -> None:
+        if self.handle:
+            sampler_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,42 @@
+// Token-pool write-back.
+//
+// "The scheduler skeleton and the offline interface", section "Preparing a
+// batch": _make_write_tuple gives each request (row = table_idx, col =
+// device_len), or col = -1 for a request that must not be written, which
+// lands harmlessly in the last column; section "_forward": the sampled
+// tokens are scattered into token_pool[rows, cols] on the device, so the
+// CPU never needs the token values.
+//
+// One thread per request; an out-of-range (row, col) skips the write and
+// raises the handle's status word (mapped pinned host memory, plain store).
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace dst {
+
+namespace {
+
+constexpr int kWriteBlock = 256;
+
+__global__ __launch_bounds__(kWriteBlock) void write_tokens_kernel(WriteArgs a) {
+    const int b = blockIdx.x * kWriteBlock + threadIdx.x;
+    if (b >= a.B) return;
+    const int64_t r = a.rows[b];
+    int64_t c = a.cols[b];
+    if (c == -1) c = a.pool_cols - 1;
+    if (r >= 0 && r < a.pool_rows && c >= 0 && c < a.pool_cols) {
+        a.pool[r * a.pool_cols + c] = a.tokens[b];
+    } else {
+        *reinterpret_cast<volatile uint32_t*>(a.status) = 1u;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_write_tokens(const WriteArgs& args, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>((args.B + kWriteBlock - 1) / kWriteBlock));
+    hipLaunchKernelGGL(write_tokens_kernel, grid, dim3(kWriteBlock), 0, stream, args);
+    return hipGetLastError();
+}
+
+}  // namespace dst

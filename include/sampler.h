@@ -1,0 +1,192 @@
+/*
+ * sampler.h -- C ABI of the MI355X (gfx950) per-step batched sampler.
+ *
+ * One decode step of an LLM serving engine ends in a sampler: it turns the
+ * [B, V] logits of the batch, plus per-request temperature / top_k / top_p,
+ * into one int32 token per request; the token is written straight back into
+ * the on-device token pool (the next step's input) and copied asynchronously
+ * to pinned host memory (for the scheduler's finish checks).  The behaviour
+ * follows the mini-sglang pages:
+ *
+ *   "The engine and the sampler", section "The sampler"   -- Sampler.prepare,
+ *       Sampler.sample, sample_torch (temperature, top-k first, top-p second,
+ *       one categorical draw; an all-greedy batch is a plain argmax);
+ *   "The engine and the sampler", section "forward_batch" -- int32 tokens, a
+ *       device copy, a non-blocking host copy and a completion event;
+ *   "The scheduler skeleton and the offline interface", sections "Preparing a
+ *       batch" (_make_write_tuple) and "_forward" -- token_pool[row, col] =
+ *       token, a column of -1 lands in the last column.
+ *
+ * Conventions for every entry point:
+ *   - Return value: 0 (SAMPLER_OK) or a negative SAMPLER_E* code.  No C++
+ *     exception crosses this boundary.  sampler_strerror() names a code;
+ *     sampler_last_error() gives the detail of the handle's last failure.
+ *   - "dev" pointers are device memory of the handle's device (e.g. from
+ *     hipMalloc or torch); "host" pointers are host memory.  The caller owns
+ *     every buffer it passes in; the library owns only the handle, a device
+ *     workspace allocated once in sampler_create, a small pinned status word
+ *     and a ring of completion events.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     sample_batch and write_tokens only enqueue work on `stream`: they never
+ *     allocate and never wait for the device.
+ *   - Argument errors that the host can see are reported synchronously and
+ *     nothing is enqueued.  Parameter *values* in device memory are never
+ *     errors: they are clamped on the device as Sampler.prepare clamps them.
+ *   - A handle is not thread-safe; use one handle per stream.  Calls on one
+ *     handle share its workspace, so calls that overlap on different streams
+ *     race.
+ */
+#ifndef DST_SAMPLER_H
+#define DST_SAMPLER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DST_API __attribute__((visibility("default")))
+#else
+#define DST_API
+#endif
+
+typedef struct dst_sampler dst_sampler;
+
+enum sampler_dtype { SAMPLER_F32 = 0, SAMPLER_BF16 = 1 };
+
+enum sampler_status {
+    SAMPLER_OK = 0,
+    SAMPLER_EINVAL = -1,      /* bad argument (null pointer, size, dtype, ...)      */
+    SAMPLER_ENOMEM = -2,      /* workspace or event allocation failed               */
+    SAMPLER_EHIP = -3,        /* a HIP runtime call or kernel launch failed         */
+    SAMPLER_ENOTPINNED = -4,  /* host_pinned_out is not page-locked host memory     */
+    SAMPLER_EDEVICE = -5,     /* a device-side bounds check fired (see write_tokens) */
+    SAMPLER_ETICKET = -6      /* unknown ticket                                      */
+};
+
+/* Largest top-k index list returned through sampler_debug.topk_idx_out. */
+#define SAMPLER_DEBUG_TOPK 64
+
+/*
+ * Optional per-call debug outputs (tests only; each field may be NULL; every
+ * non-NULL field costs extra device traffic).  All are dev pointers.
+ *   probs_out    [B, V] fp32, row-major: the final distribution r of each row
+ *                (kept masses renormalised, zero elsewhere; one-hot for greedy
+ *                rows).
+ *   kept_out     [B] int32: length of the kept prefix of the descending order.
+ *   topk_idx_out [B, 64] int32: the first min(k_eff, 64) token ids of the row
+ *                in descending-logit order (ties by ascending id), -1 padded;
+ *                for greedy rows the argmax then -1.
+ *   rand_out     [B] uint64: the Philox word the row's uniform comes from
+ *                (0 when the batch has no temperature array).
+ */
+typedef struct sampler_debug {
+    float*    probs_out;
+    int32_t*  kept_out;
+    int32_t*  topk_idx_out;
+    uint64_t* rand_out;
+} sampler_debug;
+
+/*
+ * sampler_create -- one sampler per engine ("The engine and the sampler",
+ * section "The order of initialization": Sampler(device, vocab_size) is built
+ * after the backends).
+ *   out         host: receives the handle.
+ *   device      HIP device ordinal the handle works on.
+ *   max_batch   largest B any call will pass (1 .. 1<<20); sizes the workspace.
+ *   vocab_size  V, the row length of every logits tensor (1 .. 1<<30).
+ *   logits_dtype SAMPLER_F32 or SAMPLER_BF16 (raw bf16 bit patterns).
+ *   seed        key of the counter-based generator (the engine seeds with 42).
+ * Allocates the device workspace (hipMalloc) and events; the only call that
+ * allocates.  Errors: SAMPLER_EINVAL, SAMPLER_ENOMEM, SAMPLER_EHIP.
+ */
+DST_API int sampler_create(dst_sampler** out, int device, int32_t max_batch, int32_t vocab_size,
+                   int32_t logits_dtype, uint64_t seed);
+
+/* sampler_destroy -- waits for the handle's outstanding tickets, frees its
+ * resources.  NULL is a no-op. */
+DST_API int sampler_destroy(dst_sampler* s);
+
+/*
+ * sample_batch -- one token per request ("The engine and the sampler", section
+ * "The sampler": Sampler.sample and sample_torch, with Sampler.prepare's
+ * clamps applied per row on the device).
+ *   logits      dev [B, row_stride] of the handle's dtype, row-major; only the
+ *               first V entries of each row are read.  Values must be finite.
+ *   row_stride  elements between rows, >= V.
+ *   B           rows, 0 .. max_batch (0 is a no-op).
+ *   temperature dev [B] fp32, or NULL: the whole batch is greedy (plain
+ *               row argmax, lowest index on ties).  A row whose temperature is
+ *               not above 1e-6 (0, negative, NaN) is greedy: exact argmax.
+ *   top_k       dev [B] int32 or NULL (disabled).  k < 1 or k >= V: disabled.
+ *   top_p       dev [B] fp32 or NULL (disabled).  Clamped to [1e-6, 1];
+ *               1 disables.  top-k is applied first, then top-p on the
+ *               renormalised survivors; a rank is kept while the mass before
+ *               it is < top_p, so the most likely token is always kept.
+ *   uid         dev [B] int64 request ids; required when temperature != NULL.
+ *   step        decode-step counter.  The row's uniform u comes from
+ *               Philox-4x64-10 with key (seed, 0) and counter
+ *               (uid, step, 0, 0): u = (word0 >> 40) * 2^-24.  The token is the
+ *               first id, in ascending id order, whose cumulative kept mass
+ *               exceeds u times the total kept mass.
+ *   tokens_out  dev [B] int32.
+ *   dbg         NULL, or debug outputs (see sampler_debug).
+ * Errors (synchronous, nothing enqueued): SAMPLER_EINVAL; launch failure:
+ * SAMPLER_EHIP.
+ */
+DST_API int sample_batch(dst_sampler* s, void* stream, const void* logits, int64_t row_stride,
+                 int32_t B, const float* temperature, const int32_t* top_k,
+                 const float* top_p, const int64_t* uid, uint64_t step, int32_t* tokens_out,
+                 const sampler_debug* dbg);
+
+/*
+ * write_tokens -- token_pool[rows[b], cols[b]] = tokens[b], then an async copy
+ * of tokens to host_pinned_out and a completion event ("The scheduler skeleton
+ * and the offline interface", sections "Preparing a batch" and "_forward";
+ * "The engine and the sampler", section "forward_batch").
+ *   token_pool  dev [pool_rows, pool_cols] int32, row-major.
+ *   rows, cols  dev [B] int64.  cols[b] == -1 means "do not write": it lands in
+ *               the last column.  Any other out-of-range (row, col) skips that
+ *               write and raises the handle's device flag (reported by
+ *               sampler_wait / sampler_check as SAMPLER_EDEVICE).  Rows within
+ *               one call must be distinct (one pool row per request).
+ *   tokens      dev [B] int32 (e.g. sample_batch's tokens_out).
+ *   host_pinned_out  host [B] int32 page-locked (hipHostMalloc / torch
+ *               pin_memory) or NULL (no host copy).  Must stay valid until the
+ *               ticket completes.
+ *   ticket_out  host, may be NULL: receives the ticket of this call.
+ * Errors: SAMPLER_EINVAL, SAMPLER_ENOTPINNED (synchronous); SAMPLER_EHIP.
+ */
+DST_API int write_tokens(dst_sampler* s, void* stream, int32_t* token_pool, int64_t pool_rows,
+                 int64_t pool_cols, const int64_t* rows, const int64_t* cols,
+                 const int32_t* tokens, int32_t B, int32_t* host_pinned_out,
+                 uint64_t* ticket_out);
+
+/*
+ * sampler_wait -- block until the ticket's work (and its host copy) is done:
+ * copy_done_event.synchronize() of "The engine and the sampler", section
+ * "forward_batch".  Returns SAMPLER_EDEVICE if a device bounds check has
+ * fired since the last sampler_check, SAMPLER_ETICKET for a ticket never
+ * issued.  Tickets older than the event ring (256) wait on a later ticket.
+ */
+DST_API int sampler_wait(dst_sampler* s, uint64_t ticket);
+
+/* sampler_query -- 1 if the ticket is done, 0 if pending, <0 on error. */
+DST_API int sampler_query(dst_sampler* s, uint64_t ticket);
+
+/* sampler_check -- waits for the whole device, returns SAMPLER_EDEVICE if a
+ * device bounds check fired since the last check, and clears the flag. */
+DST_API int sampler_check(dst_sampler* s);
+
+/* sampler_strerror -- static string for a status code. */
+DST_API const char* sampler_strerror(int code);
+
+/* sampler_last_error -- detail of the handle's last failure ("" if none). */
+DST_API const char* sampler_last_error(dst_sampler* s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DST_SAMPLER_H */

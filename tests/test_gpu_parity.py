@@ -1,0 +1,196 @@
+"""Parity of the HIP sampler with the fp64 oracle, through the C ABI.
+
+Every case prints its name before touching the GPU.  Small cases compare
+every row and every probability; the full-size workloads compare every row's
+token, kept length, top-k list and Philox word, and the probabilities of a
+sample of rows.
+"""
+import numpy as np
+import pytest
+import scipy.stats
+import torch
+
+import decode_step_token_amd as dst
+import workloads as wl
+from tests.parity import compare, log, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    dst.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _check(w, **kw):
+    log(f"case {w.name} B={w.B} V={w.V} dtype={w.dtype} step={w.step}")
+    gpu = run_gpu(w, **{k: v for k, v in kw.items() if k in ("pad", "debug")})
+    ref = run_oracle(w)
+    stats = compare(w, gpu, ref, check_probs_rows=kw.get("probs_rows"))
+    log(f"  ok {stats}")
+    return gpu, ref
+
+
+def test_c0_mixed_batch():
+    gpu, ref = _check(wl.c0())
+    assert [r.greedy for r in ref] == [True, True, False, False]
+
+
+def test_c0_permuted():
+    a, _ = _check(wl.c0())
+    b, _ = _check(wl.c0_permuted())
+    perm = [2, 0, 3, 1]
+    assert list(b["tokens"]) == [a["tokens"][i] for i in perm]
+
+
+def test_c1_all_greedy_with_ties():
+    w = wl.c1()
+    gpu, ref = _check(w)
+    for b, i_star, j in w.meta["ties"]:
+        assert gpu["tokens"][b] == min(i_star, j)
+    assert np.array_equal(gpu["tokens"], np.argmax(w.logits, axis=1))
+
+
+@pytest.mark.parametrize("V,dtype,pad", [
+    (1, "f32", 0), (2, "bf16", 0), (63, "f32", 1), (64, "bf16", 0), (1000, "f32", 0),
+    (1023, "bf16", 3), (4097, "f32", 1), (5000, "bf16", 0), (33000, "f32", 0),
+])
+def test_tiny_mixed_batches(V, dtype, pad):
+    rng = np.random.default_rng(V * 7 + pad)
+    w = wl.tiny(rng, 48, V, dtype)
+    _check(w, pad=pad)
+
+
+def test_all_equal_and_signed_zero_rows():
+    rng = np.random.default_rng(11)
+    w = wl.tiny(rng, 16, 300, "f32")
+    w.logits[0:4] = 0.0
+    w.logits[2, ::2] = -0.0
+    w.logits[4:8] = 1.5
+    w.logits[8, 100:] = w.logits[8].max()
+    w.temperature[:8] = np.float32(0.9)
+    w.top_k[:8] = np.array([-1, 5, 150, 1, -1, 20, 299, 0], dtype=np.int32)
+    w.top_p[:8] = np.array([0.5, 1.0, 0.3, 0.9, 0.95, 0.5, 0.999, 1.0], dtype=np.float32)
+    _check(w)
+
+
+def test_extreme_temperatures_and_parameters():
+    rng = np.random.default_rng(12)
+    w = wl.tiny(rng, 32, 2000, "f32", scale=6.0)
+    w.temperature[:] = np.array([1.1e-6, 2e-6, 1e-5, 1e-3, 0.05, 20.0, 1e4, float("nan")] * 4,
+                                dtype=np.float32)
+    w.top_p[::3] = np.float32(float("nan"))
+    w.top_k[::5] = np.int32(-(2 ** 31))
+    _check(w)
+
+
+def test_greedy_batch_without_temperature_bf16():
+    rng = np.random.default_rng(13)
+    w = wl.tiny(rng, 100, 7000, "bf16")
+    w.temperature = None
+    _check(w)
+
+
+def test_c2_full():
+    _check(wl.c2(), probs_rows=set(range(0, 256, 17)))
+
+
+def test_c3_full():
+    _check(wl.c3(), probs_rows=set(range(0, 256, 13)))
+
+
+@pytest.mark.parametrize("step,half_greedy", [(0, False), (1, False), (63, False), (0, True)])
+def test_c4_decode_steps(step, half_greedy):
+    _check(wl.c4(step, half_greedy), probs_rows=set(range(0, 512, 61)))
+
+
+def test_repeat_and_recreate_are_identical():
+    w = wl.tiny(np.random.default_rng(14), 64, 5000, "f32")
+    log("case repeat/recreate")
+    a = run_gpu(w, debug=False)
+    b = run_gpu(w, debug=False)
+    s = dst.Sampler(0, 64, 5000, "f32", w.seed)
+    c = run_gpu(w, sampler=s, debug=False)
+    d = run_gpu(w, sampler=s, debug=False)
+    s.close()
+    for o in (b, c, d):
+        assert np.array_equal(a["tokens"], o["tokens"])
+
+
+def test_draw_distribution_chi_square():
+    """Many independent draws (distinct uids) from one row match r."""
+    rng = np.random.default_rng(15)
+    V, B = 1024, 4096
+    x = rng.normal(0, 2, V).astype(np.float32)
+    w = wl.Workload("chi2", "f32", np.tile(x, (B, 1)), np.full(B, 0.7, np.float32),
+                    np.full(B, 50, np.int32), np.full(B, 0.9, np.float32),
+                    np.arange(B, dtype=np.int64) * 7919, 3, np.zeros((B, 2), np.int32),
+                    np.arange(B, dtype=np.int64), np.zeros(B, np.int64))
+    log("case chi-square")
+    gpu = run_gpu(w, debug=False)
+    r = run_oracle(w, rows=[0])[0].r
+    support = np.flatnonzero(r > 0)
+    counts = np.bincount(gpu["tokens"], minlength=V)
+    assert counts[r == 0].sum() == 0
+    expected = r[support] * B
+    big = expected >= 5
+    obs = np.append(counts[support][big], counts[support][~big].sum())
+    exp = np.append(expected[big], expected[~big].sum())
+    keep = exp > 0
+    stat, pval = scipy.stats.chisquare(obs[keep], exp[keep] * obs[keep].sum() / exp[keep].sum())
+    log(f"  chi2={stat:.1f} p={pval:.3g} support={len(support)}")
+    assert pval > 1e-4
+
+
+def test_write_tokens_errors_and_tickets():
+    log("case write_tokens errors")
+    s = dst.Sampler(0, 8, 100, "f32")
+    pool = torch.zeros((4, 10), dtype=torch.int32, device="cuda")
+    toks = torch.arange(3, dtype=torch.int32, device="cuda") + 5
+    rows = torch.tensor([0, 1, 2], dtype=torch.int64, device="cuda")
+    cols = torch.tensor([-1, 3, 9], dtype=torch.int64, device="cuda")
+    host = torch.zeros(3, dtype=torch.int32).pin_memory()
+    t = s.write(pool, rows, cols, toks, host)
+    s.wait(t)
+    assert pool[0, 9].item() == 5 and pool[1, 3].item() == 6 and pool[2, 9].item() == 7
+    assert host.tolist() == [5, 6, 7]
+    assert s.query(t)
+    # out of range: skipped, reported by wait and check
+    bad_cols = torch.tensor([10, -2, 0], dtype=torch.int64, device="cuda")
+    before = pool.clone()
+    t2 = s.write(pool, rows, bad_cols, toks)
+    with pytest.raises(dst.SamplerError) as e:
+        s.wait(t2)
+    assert e.value.code == -5
+    with pytest.raises(dst.SamplerError):
+        s.check()
+    s.check()  # cleared
+    assert torch.equal(pool[:, 1:], before[:, 1:]) and pool[2, 0].item() == 7
+    # pageable host memory is refused before anything is enqueued
+    with pytest.raises(dst.SamplerError) as e:
+        s.write(pool, rows, cols, toks, torch.zeros(3, dtype=torch.int32))
+    assert e.value.code == -4
+    with pytest.raises(dst.SamplerError) as e:
+        s.wait(10 ** 6)
+    assert e.value.code == -6
+    s.close()
+
+
+def test_argument_errors():
+    log("case argument errors")
+    s = dst.Sampler(0, 4, 100, "f32")
+    x = torch.zeros((5, 100), device="cuda")
+    with pytest.raises(dst.SamplerError) as e:
+        s.sample(x)                                   # B > max_batch
+    assert e.value.code == -1
+    y = torch.zeros((2, 100), device="cuda")
+    with pytest.raises(dst.SamplerError):
+        s.sample(y, temperature=torch.ones(2, device="cuda"))   # uid missing
+    with pytest.raises(dst.SamplerError):
+        s.sample(y, row_stride=50)
+    out = s.sample(y[:0])                             # B == 0 is a no-op
+    assert out.numel() == 0
+    s.close()
