@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libd
 SAMPLER_F32 = 0
 SAMPLER_BF16 = 1
 SAMPLER_DEBUG_TOPK = 64
+SAMPLER_DEBUG_FORCE_EXACT = 1
 
 STATUS = {0: "SAMPLER_OK", -1: "SAMPLER_EINVAL", -2: "SAMPLER_ENOMEM", -3: "SAMPLER_EHIP",
           -4: "SAMPLER_ENOTPINNED", -5: "SAMPLER_EDEVICE", -6: "SAMPLER_ETICKET"}
@@ -38,7 +39,8 @@ class SamplerError(RuntimeError):
 
 class SamplerDebug(ctypes.Structure):
     _fields_ = [("probs_out", ctypes.c_void_p), ("kept_out", ctypes.c_void_p),
-                ("topk_idx_out", ctypes.c_void_p), ("rand_out", ctypes.c_void_p)]
+                ("topk_idx_out", ctypes.c_void_p), ("rand_out", ctypes.c_void_p),
+                ("flags", ctypes.c_uint32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -143,6 +145,7 @@ def sample_batch(handle, logits: torch.Tensor, temperature=None, top_k=None, top
                           ("topk_idx_out", torch.int32), ("rand_out", torch.int64)):
             t = debug.get(field)
             setattr(dbg, field, None if t is None else _ptr(t, field, dt, None, dev).value)
+        dbg.flags = SAMPLER_DEBUG_FORCE_EXACT if debug.get("force_exact") else 0
     code = load().sample_batch(
         handle, _stream(stream), ctypes.c_void_p(logits.data_ptr()), stride, B,
         _ptr(temperature, "temperature", torch.float32, B, dev),

@@ -19,8 +19,9 @@ BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdst_sampler.so")
 
-SOURCES = ["argmax.hip", "sample_exact.hip", "write_tokens.hip", "sampler_api.hip"]
-HEADERS = ["device_common.hpp", "kernels.hpp"]
+SOURCES = ["argmax.hip", "sample_exact.hip", "sample_stream.hip", "write_tokens.hip",
+           "sampler_api.hip"]
+HEADERS = ["device_common.hpp", "kernels.hpp", "exact_path.hpp"]
 
 ARCH = "gfx950"
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

@@ -15,6 +15,25 @@ constexpr int kDtypeBF16 = 1;
 constexpr float kMinT = 1e-6f;
 constexpr float kMinP = 1e-6f;
 
+// ------------------------------------------------------------ loads --
+
+// Load through the global address space (global_load_*, not flat_load_*):
+// flat loads also count against the LDS wait counter, which serialises the
+// streaming loop against its LDS traffic.
+template <typename T>
+__device__ __forceinline__ T ld_global(const void* p) {
+    return *reinterpret_cast<const __attribute__((address_space(1))) T*>(
+        reinterpret_cast<uintptr_t>(p));
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load (the HIP vector classes cannot be built from a global reference).
+__device__ __forceinline__ uint4 ld_global_u4(const void* p) {
+    const u32x4_t v = ld_global<u32x4_t>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---------------------------------------------------------------- values --
 
 // Order-preserving 32-bit key of a float: larger float -> larger key; -0.0
@@ -42,12 +61,13 @@ struct Elem<kDtypeF32> {
     using scalar_t = float;
     static constexpr int kVec = 4;  // 16-byte loads
     __device__ static __forceinline__ float at(const void* row, int64_t i) {
-        return static_cast<const float*>(row)[i];
+        return ld_global<float>(static_cast<const float*>(row) + i);
     }
     // Loads kVec consecutive values starting at i (16-byte aligned).
     __device__ static __forceinline__ void vec(const void* row, int64_t i, float* out) {
-        float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(row) + i);
-        out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+        const uint4 v = ld_global_u4(static_cast<const float*>(row) + i);
+        out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+        out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
     }
 };
 
@@ -56,10 +76,10 @@ struct Elem<kDtypeBF16> {
     using scalar_t = uint16_t;
     static constexpr int kVec = 8;  // 16-byte loads
     __device__ static __forceinline__ float at(const void* row, int64_t i) {
-        return bf16_bits_f32(static_cast<const uint16_t*>(row)[i]);
+        return bf16_bits_f32(ld_global<uint16_t>(static_cast<const uint16_t*>(row) + i));
     }
     __device__ static __forceinline__ void vec(const void* row, int64_t i, float* out) {
-        uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + i);
+        const uint4 v = ld_global_u4(static_cast<const uint16_t*>(row) + i);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -89,12 +109,12 @@ __device__ __forceinline__ RowParams row_params(const float* temperature, const 
         r.greedy = true; r.T = kMinT; r.k = 1; r.p = 1.0f; r.top_p = false;
         return r;
     }
-    const float t = temperature[b];
+    const float t = ld_global<float>(temperature + b);
     r.greedy = !(t > kMinT);
     r.T = r.greedy ? kMinT : t;
-    int k = top_k ? top_k[b] : 0;
+    int k = top_k ? ld_global<int32_t>(top_k + b) : 0;
     r.k = (k < 1 || k >= V) ? V : k;
-    float p = top_p ? top_p[b] : 1.0f;
+    float p = top_p ? ld_global<float>(top_p + b) : 1.0f;
     p = fminf(fmaxf(p, kMinP), 1.0f);
     r.p = p;
     r.top_p = p < 1.0f;
@@ -142,6 +162,133 @@ __device__ __forceinline__ uint64_t request_word(uint64_t seed, int64_t uid, uin
 // 24-bit dyadic uniform in [0, 1), exact in float and double.
 __device__ __forceinline__ double uniform24(uint64_t word) {
     return static_cast<double>(word >> 40) * (1.0 / 16777216.0);
+}
+
+// ------------------------------------------------- DPP wave64 reductions --
+// Cross-lane data movement through DPP (no LDS round trip): quad swaps, row
+// half-mirror and mirror combine within a 16-lane row, then row_bcast15 /
+// row_bcast31 fold the four rows so that lane 63 holds the result, which is
+// read back into a scalar register.
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v),
+                                                             CTRL, ROW_MASK, 0xf, false));
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f32(float old, float v) {
+    return __uint_as_float(dpp_u32<CTRL, ROW_MASK>(__float_as_uint(old), __float_as_uint(v)));
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_f64(double old, double v) {
+    const uint64_t o = static_cast<uint64_t>(__double_as_longlong(old));
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint32_t lo = dpp_u32<CTRL, ROW_MASK>(static_cast<uint32_t>(o), static_cast<uint32_t>(b));
+    const uint32_t hi = dpp_u32<CTRL, ROW_MASK>(static_cast<uint32_t>(o >> 32), static_cast<uint32_t>(b >> 32));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+constexpr int kDppXor1 = 0xb1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4e;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
+
+// Maximum over the 64 lanes, returned wave-uniform.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = fmaxf(v, dpp_f32<kDppXor1>(v, v));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v, v));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v, v));
+    v = fmaxf(v, dpp_f32<kDppMirror>(v, v));
+    v = fmaxf(v, dpp_f32<kDppBcast15, 0xa>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<kDppBcast31, 0xc>(-INFINITY, v));
+    return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(__float_as_uint(v)), 63)));
+}
+
+// Sum over the 64 lanes, returned wave-uniform.
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+    v += dpp_f64<kDppXor1>(v, v);
+    v += dpp_f64<kDppXor2>(v, v);
+    v += dpp_f64<kDppHalfMirror>(v, v);
+    v += dpp_f64<kDppMirror>(v, v);
+    v += dpp_f64<kDppBcast15, 0xa>(0.0, v);
+    v += dpp_f64<kDppBcast31, 0xc>(0.0, v);
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b)), 63));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b >> 32)), 63));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// Inclusive prefix sum over the 64 lanes (lane order) through DPP: shifts of
+// 1, 2, 4, 8 within each 16-lane row, then the row_bcast15 / row_bcast31
+// carries across rows.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32_zero(uint32_t v) {
+    // lanes without a source read 0 (bound_ctrl)
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, 0xf, true));
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_f64_zero(double v) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint32_t lo = dpp_u32_zero<CTRL, ROW_MASK>(static_cast<uint32_t>(b));
+    const uint32_t hi = dpp_u32_zero<CTRL, ROW_MASK>(static_cast<uint32_t>(b >> 32));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+constexpr int kDppShr1 = 0x111;
+constexpr int kDppShr2 = 0x112;
+constexpr int kDppShr4 = 0x114;
+constexpr int kDppShr8 = 0x118;
+
+__device__ __forceinline__ uint32_t wave_scan_u32_dpp(uint32_t v) {
+    v += dpp_u32_zero<kDppShr1>(v);
+    v += dpp_u32_zero<kDppShr2>(v);
+    v += dpp_u32_zero<kDppShr4>(v);
+    v += dpp_u32_zero<kDppShr8>(v);
+    v += dpp_u32_zero<kDppBcast15, 0xa>(v);
+    v += dpp_u32_zero<kDppBcast31, 0xc>(v);
+    return v;
+}
+
+__device__ __forceinline__ double wave_scan_f64_dpp(double v) {
+    v += dpp_f64_zero<kDppShr1>(v);
+    v += dpp_f64_zero<kDppShr2>(v);
+    v += dpp_f64_zero<kDppShr4>(v);
+    v += dpp_f64_zero<kDppShr8>(v);
+    v += dpp_f64_zero<kDppBcast15, 0xa>(v);
+    v += dpp_f64_zero<kDppBcast31, 0xc>(v);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint32_t lo = readlane_u32(static_cast<uint32_t>(b), lane);
+    const uint32_t hi = readlane_u32(static_cast<uint32_t>(b >> 32), lane);
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+    v = max(v, dpp_u32<kDppXor1>(v, v));
+    v = max(v, dpp_u32<kDppXor2>(v, v));
+    v = max(v, dpp_u32<kDppHalfMirror>(v, v));
+    v = max(v, dpp_u32<kDppMirror>(v, v));
+    v = max(v, dpp_u32<kDppBcast15, 0xa>(0u, v));
+    v = max(v, dpp_u32<kDppBcast31, 0xc>(0u, v));
+    return readlane_u32(v, 63);
+}
+
+// Rank of this lane among the set bits of `mask` below it.
+__device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
 // ------------------------------------------------------ wave64 reductions --

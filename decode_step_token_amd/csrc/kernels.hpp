@@ -51,6 +51,7 @@ struct WriteArgs {
 hipError_t launch_argmax(const ArgmaxArgs& args, int dtype, hipStream_t stream);
 void argmax_plan(int B, int V, int dtype, int* chunks, int* chunk_len);
 hipError_t launch_sample_exact(const SampleArgs& args, int dtype, hipStream_t stream);
+hipError_t launch_sample_stream(const SampleArgs& args, int dtype, hipStream_t stream);
 hipError_t launch_write_tokens(const WriteArgs& args, hipStream_t stream);
 
 }  // namespace dst

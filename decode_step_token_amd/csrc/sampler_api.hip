@@ -13,7 +13,7 @@
 #include <new>
 #include <string>
 
-#include "../../include/sampler.h"
+#include "sampler.h"
 #include "kernels.hpp"
 
 namespace {
@@ -191,7 +191,10 @@ int sample_batch(dst_sampler* s, void* stream, const void* logits, int64_t row_s
             a.topk_idx_out = dbg->topk_idx_out;
             a.rand_out = dbg->rand_out;
         }
-        e = dst::launch_sample_exact(a, s->dtype, st);
+        if (dbg && (dbg->flags & SAMPLER_DEBUG_FORCE_EXACT))
+            e = dst::launch_sample_exact(a, s->dtype, st);
+        else
+            e = dst::launch_sample_stream(a, s->dtype, st);
     }
     if (e != hipSuccess) return fail(s, SAMPLER_EHIP, "sample_batch: launch", e);
     return SAMPLER_OK;

@@ -68,6 +68,10 @@ enum sampler_status {
 /* Largest top-k index list returned through sampler_debug.topk_idx_out. */
 #define SAMPLER_DEBUG_TOPK 64
 
+/* sampler_debug.flags: run every row through the exact multi-pass path
+ * (re-reads each row several times) instead of the single-pass kernel. */
+#define SAMPLER_DEBUG_FORCE_EXACT 1u
+
 /*
  * Optional per-call debug outputs (tests only; each field may be NULL; every
  * non-NULL field costs extra device traffic).  All are dev pointers.
@@ -80,12 +84,14 @@ enum sampler_status {
  *                for greedy rows the argmax then -1.
  *   rand_out     [B] uint64: the Philox word the row's uniform comes from
  *                (0 when the batch has no temperature array).
+ *   flags        host value: 0, or SAMPLER_DEBUG_FORCE_EXACT.
  */
 typedef struct sampler_debug {
     float*    probs_out;
     int32_t*  kept_out;
     int32_t*  topk_idx_out;
     uint64_t* rand_out;
+    uint32_t  flags;
 } sampler_debug;
 
 /*

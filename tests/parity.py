@@ -44,7 +44,7 @@ def opt(a, dtype):
 
 
 def run_gpu(w: Workload, sampler: dst.Sampler = None, debug: bool = True, pad: int = 0,
-            host: bool = True, logits_dev: torch.Tensor = None):
+            host: bool = True, logits_dev: torch.Tensor = None, force_exact: bool = False):
     """Run sample_batch + write_tokens for one step; returns numpy results."""
     own = sampler is None
     if own:
@@ -62,6 +62,8 @@ def run_gpu(w: Workload, sampler: dst.Sampler = None, debug: bool = True, pad: i
                    "kept_out": torch.full((B,), -7, dtype=torch.int32, device="cuda"),
                    "topk_idx_out": torch.full((B, 64), -7, dtype=torch.int32, device="cuda"),
                    "rand_out": torch.full((B,), -7, dtype=torch.int64, device="cuda")}
+        if force_exact:
+            dbg = dict(dbg or {}, force_exact=True)
         toks = sampler.sample(logits, temperature=T, top_k=k, top_p=p, uid=uid, step=w.step,
                               debug=dbg)
         pool = torch.from_numpy(w.pool.copy()).cuda()
@@ -74,7 +76,8 @@ def run_gpu(w: Workload, sampler: dst.Sampler = None, debug: bool = True, pad: i
                "host": None if host_out is None else host_out.numpy().copy()}
         if dbg:
             for name, t in dbg.items():
-                out[name] = t.cpu().numpy()
+                if isinstance(t, torch.Tensor):
+                    out[name] = t.cpu().numpy()
         return out
     finally:
         if own:

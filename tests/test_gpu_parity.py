@@ -26,8 +26,9 @@ def _gpu():
 
 
 def _check(w, **kw):
-    log(f"case {w.name} B={w.B} V={w.V} dtype={w.dtype} step={w.step}")
-    gpu = run_gpu(w, **{k: v for k, v in kw.items() if k in ("pad", "debug")})
+    log(f"case {w.name} B={w.B} V={w.V} dtype={w.dtype} step={w.step} "
+        f"{'exact path' if kw.get('force_exact') else ''}")
+    gpu = run_gpu(w, **{k: v for k, v in kw.items() if k in ("pad", "debug", "force_exact")})
     ref = run_oracle(w)
     stats = compare(w, gpu, ref, check_probs_rows=kw.get("probs_rows"))
     log(f"  ok {stats}")
@@ -91,6 +92,38 @@ def test_greedy_batch_without_temperature_bf16():
     rng = np.random.default_rng(13)
     w = wl.tiny(rng, 100, 7000, "bf16")
     w.temperature = None
+    _check(w)
+
+
+@pytest.mark.parametrize("V,dtype", [(1000, "f32"), (5000, "bf16"), (33000, "f32")])
+def test_tiny_mixed_batches_exact_path(V, dtype):
+    w = wl.tiny(np.random.default_rng(V * 11), 48, V, dtype)
+    _check(w, force_exact=True)
+
+
+def test_c3_exact_path():
+    _check(wl.c3(), probs_rows=set(range(0, 256, 29)), force_exact=True)
+
+
+def test_c3_without_debug_outputs():
+    """The production launch (no debug buffers) gives the same tokens."""
+    w = wl.c3()
+    log("case c3 without debug outputs")
+    a = run_gpu(w, debug=False)
+    b = run_gpu(w, debug=True)
+    assert np.array_equal(a["tokens"], b["tokens"])
+    assert np.array_equal(a["pool"], b["pool"])
+
+
+def test_flat_rows_fall_back_to_exact():
+    """Very flat rows with top-p only: the nucleus is far larger than the
+    candidate buffer, so the single-pass kernel must hand them to the exact
+    path and still match the oracle."""
+    rng = np.random.default_rng(16)
+    w = wl.tiny(rng, 8, 40000, "bf16", scale=0.5)
+    w.temperature[:] = np.float32(2.0)
+    w.top_k[:] = -1
+    w.top_p[:] = np.array([0.9, 0.5, 0.99, 0.999, 0.7, 0.95, 0.3, 0.8], dtype=np.float32)
     _check(w)
 
 
