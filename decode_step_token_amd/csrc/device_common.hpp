@@ -285,6 +285,29 @@ __device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
     return readlane_u32(v, 63);
 }
 
+// Maximum of a 64-bit value over the 64 lanes (wave-uniform result).
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+    auto step = [](uint64_t x, uint32_t olo, uint32_t ohi) {
+        const uint64_t o = (static_cast<uint64_t>(ohi) << 32) | olo;
+        return o > x ? o : x;
+    };
+    uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+    v = step(v, dpp_u32<kDppXor1>(lo, lo), dpp_u32<kDppXor1>(hi, hi));
+    lo = static_cast<uint32_t>(v); hi = static_cast<uint32_t>(v >> 32);
+    v = step(v, dpp_u32<kDppXor2>(lo, lo), dpp_u32<kDppXor2>(hi, hi));
+    lo = static_cast<uint32_t>(v); hi = static_cast<uint32_t>(v >> 32);
+    v = step(v, dpp_u32<kDppHalfMirror>(lo, lo), dpp_u32<kDppHalfMirror>(hi, hi));
+    lo = static_cast<uint32_t>(v); hi = static_cast<uint32_t>(v >> 32);
+    v = step(v, dpp_u32<kDppMirror>(lo, lo), dpp_u32<kDppMirror>(hi, hi));
+    lo = static_cast<uint32_t>(v); hi = static_cast<uint32_t>(v >> 32);
+    v = step(v, dpp_u32<kDppBcast15, 0xa>(0u, lo), dpp_u32<kDppBcast15, 0xa>(0u, hi));
+    lo = static_cast<uint32_t>(v); hi = static_cast<uint32_t>(v >> 32);
+    v = step(v, dpp_u32<kDppBcast31, 0xc>(0u, lo), dpp_u32<kDppBcast31, 0xc>(0u, hi));
+    lo = readlane_u32(static_cast<uint32_t>(v), 63);
+    hi = readlane_u32(static_cast<uint32_t>(v >> 32), 63);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // Rank of this lane among the set bits of `mask` below it.
 __device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),

@@ -11,11 +11,14 @@
 // What one read of the row leaves behind:
 //   * the row maximum and its lowest index, from per-tile lane maxima (the
 //     argmax bookkeeping only runs when a lane's tile beats its running best);
-//   * for rows without top-k: one fp64 softmax sum per tile (1024 fp32 or
-//     2048 bf16 logits), relative to the wave's running maximum.  The
-//     exponent argument (x - ref) * log2(e)/T is formed in fp64 and only its
-//     fraction goes through v_exp_f32, so each weight carries ~1e-7 relative
-//     error however far x lies below the maximum;
+//   * for rows without top-k: one softmax sum per tile (1024 fp32 or 2048
+//     bf16 logits) relative to the tile's own maximum tref, with fp32
+//     arguments (x - tref) * log2(e)/T through v_exp_f32, rescaled to the row
+//     maximum in fp64 at the end.  (x - tref) is exact for every logit within
+//     a factor two of tref, which carries the tile's mass, so the normaliser
+//     stays within ~2e-7 of the fp64 sum on the workloads here (an argument
+//     taken relative to the row maximum in one fp32 expression is off by up
+//     to 2.5e-6);
 //   * for rows with top-k or top-p: every logit >= theta, with its index, in a
 //     wave-private LDS region (ballot + mbcnt compaction, a scalar counter, no
 //     LDS atomics).  theta is fixed after the first tile of every wave: the
@@ -53,7 +56,7 @@ constexpr int kRegion = 512;               // candidate entries per wave
 constexpr int kCap = kWaves * kRegion;     // 8192
 constexpr int kMaxTiles = 512;
 constexpr int kList = 64;
-constexpr int kTopPTarget = 2500;          // aimed-at candidate count for top-p rows
+constexpr int kTopPTarget = 1500;          // aimed-at candidate count for top-p rows
 
 enum Mode { kArgmax = 0, kTopK = 1, kTopP = 2, kFull = 3 };
 
@@ -85,7 +88,7 @@ struct Smem {
 template <int DT>
 struct TileIO {
     static constexpr int VEC = Elem<DT>::kVec;
-    static constexpr int U = 4;                       // 16-byte loads per lane
+    static constexpr int U = DT == kDtypeF32 ? 4 : 2;  // 16-byte loads per lane per tile
     static constexpr int Q = U * VEC;                 // elements per lane per tile
     static constexpr int TILE = kWave * Q;            // contiguous elements per tile
 
@@ -309,8 +312,8 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     // ------------------------------------------------------------ stream --
     float best_x = -INFINITY;
     int best_t = -1, best_q = 0;
-    float m_w = -INFINITY;
     float theta = INFINITY;
+    const float c32 = static_cast<float>(c);
     uint32_t cnt = 0;                 // this wave's region fill (wave-uniform)
 
     auto process = [&](const uint4* raw, int t) {
@@ -326,33 +329,39 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             best_q = qq;
         }
         if (want_z) {
-            if (__ballot(tmax > m_w) != 0) m_w = fmaxf(m_w, wave_max_dpp(tmax));
-            const double refc = static_cast<double>(m_w) * c;
-            double s = 0.0;
+            // tile-local reference: (x - tref) is exact for the logits that
+            // carry the tile's mass, so fp32 arguments are accurate here; the
+            // tile sum is rescaled to the row maximum in fp64 at the end
+            const float tref = wave_max_dpp(tmax);
+            float s = 0.0f;
 #pragma unroll
-            for (int q = 0; q < Q; ++q) s += fast_weight(IO::get(raw, q), refc, c);
-            s = wave_sum_dpp(s);
+            for (int q = 0; q < Q; ++q) s += __builtin_amdgcn_exp2f((IO::get(raw, q) - tref) * c32);
+            const double st = wave_sum_dpp(static_cast<double>(s));
             if (lane == 0) {
-                ss.tref[t] = m_w;
-                ss.tsum[t] = s;
+                ss.tref[t] = tref;
+                ss.tsum[t] = st;
             }
         }
         if (want_cand && __ballot(tmax >= theta) != 0) {
-            const int rbase = wid * kRegion;
+            // lane masks, one DPP prefix scan for the slots, predicated writes
+            uint32_t mask = 0;
 #pragma unroll
-            for (int q = 0; q < Q; ++q) {
-                const float x = IO::get(raw, q);
-                const bool in = x >= theta;
-                const uint64_t bal = __ballot(in);
-                if (bal) {
-                    const uint32_t pos = cnt + lane_rank(bal);
-                    if (in && pos < kRegion) {
-                        ss.ckey[rbase + pos] = f32_key(x);
-                        ss.cidx[rbase + pos] = IO::index(t, lane, q);
+            for (int q = 0; q < Q; ++q) mask |= IO::get(raw, q) >= theta ? (1u << q) : 0u;
+            const uint32_t mine = static_cast<uint32_t>(__popc(mask));
+            const uint32_t incl = wave_scan_u32_dpp(mine);
+            const uint32_t tot = readlane_u32(incl, kWave - 1);
+            if (cnt + tot <= static_cast<uint32_t>(kRegion)) {
+                uint32_t pos = static_cast<uint32_t>(wid * kRegion) + cnt + incl - mine;
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    if (mask & (1u << q)) {
+                        ss.ckey[pos] = f32_key(IO::get(raw, q));
+                        ss.cidx[pos] = IO::index(t, lane, q);
+                        ++pos;
                     }
-                    cnt += static_cast<uint32_t>(__popcll(bal));
                 }
             }
+            cnt += tot;
         }
     };
 
@@ -436,7 +445,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             const uint32_t idx = best_q >= 0 ? IO::index(best_t, lane, best_q) : static_cast<uint32_t>(best_t);
             pk = (static_cast<uint64_t>(f32_key(best_x)) << 32) | static_cast<uint64_t>(0xffffffffu - idx);
         }
-        pk = wave_max(pk);
+        pk = wave_max_u64_dpp(pk);
         __syncthreads();
         if (lane == 0) {
             ss.wbest[wid] = pk;
