@@ -30,6 +30,10 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "sampled rows/sec and achieved HBM GB/s (% of peak) at B=256, V=151936"
 PARAM_BYTES_PER_ROW = 4 + 4 + 4 + 8 + 4   # T, top_k, top_p, uid read; token written
 WRITE_BYTES_PER_ROW = 8 + 8 + 4 + 4       # row, col, token read; pool cell written
+# calibration copy for the HBM byte counters: torch's elementwise negation of
+# one fp32 logits buffer into another (one read and one write of each byte)
+COPY_KERNEL_NEEDLE = "neg_kernel"
+COPY_BYTES = 256 * 151936 * 4
 
 
 def eprint(*a):
@@ -62,6 +66,63 @@ def load_traffic(kernel: str, workload: str):
     return None
 
 
+def write_traffic(fetch_csv: str, write_csv: str, kernel: str, workload: str, command: str):
+    """Turn two rocprofv3 --pmc counter files (FETCH_SIZE, then WRITE_SIZE, KiB
+    per dispatch) into HBM bytes per launch of the sampler kernel, scaled by
+    what the same counters read for the plain copy kernel that the
+    --calibrate-copy run launches (known bytes read and written), and record
+    them in profiles/traffic.json with the digest of the kernel sources."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path, newline="") as f:
+            for rec in csv.DictReader(f):
+                if rec.get("Counter_Name") != counter:
+                    continue
+                vals.setdefault(rec["Kernel_Name"], []).append(float(rec["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(vals, needle):
+        names = [n for n in vals if needle in n]
+        if len(names) != 1:
+            raise SystemExit(f"expected one kernel matching {needle!r}, found {names}")
+        v = vals[names[0]]
+        return names[0], sum(v) / len(v), len(v)
+
+    kname, kf, nf = pick(fetch, "sample_stream_kernel")
+    _, kw, nw = pick(write, "sample_stream_kernel")
+    cname, cf, _ = pick(fetch, COPY_KERNEL_NEEDLE)
+    _, cw, _ = pick(write, COPY_KERNEL_NEEDLE)
+    fscale = cf * 1024.0 / COPY_BYTES
+    wscale = cw * 1024.0 / COPY_BYTES
+    rec = {
+        "kernel_name": kname,
+        "fetch_kib_per_launch": kf, "write_kib_per_launch": kw, "dispatches": [nf, nw],
+        "copy_kernel": cname, "copy_bytes_each_way": COPY_BYTES,
+        "copy_fetch_kib": cf, "copy_write_kib": cw,
+        "fetch_scale": fscale, "write_scale": wscale,
+        "fetch_bytes_per_launch": kf * 1024.0 / fscale,
+        "write_bytes_per_launch": kw * 1024.0 / wscale,
+        "bytes_per_launch": kf * 1024.0 / fscale + kw * 1024.0 / wscale,
+        "sources_digest": kernel_sources_digest(),
+        "command": command,
+    }
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data[f"{kernel}@{workload}"] = rec
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
 def cpu_baseline(w, seconds: float):
     import oracle
     t0 = time.perf_counter()
@@ -85,7 +146,18 @@ def main():
     ap.add_argument("--buffers", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also launch the plain copy kernel the byte counters are scaled by")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="record counter-measured bytes per launch in profiles/traffic.json")
+    ap.add_argument("--traffic-command", default="",
+                    help="with --write-traffic: the profiling command, stored with the figures")
     args = ap.parse_args()
+
+    if args.write_traffic:
+        write_traffic(args.write_traffic[0], args.write_traffic[1], "sample_batch", "c3",
+                      args.traffic_command)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this sampler runs on one GPU; --gpus {args.gpus} is not supported "
@@ -155,6 +227,14 @@ def main():
     kernel_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     sampler.check()
     sampler.close()
+
+    if args.calibrate_copy:
+        eprint("bench: calibration copy (elementwise negation of one logits buffer)")
+        dst_buf = torch.empty_like(bufs[0])
+        for _ in range(3):
+            torch.neg(bufs[0], out=dst_buf)
+        torch.cuda.synchronize()
+        del dst_buf
 
     ms_per_step = elapsed * 1e3 / args.steps
     avg_kernel_ms = float(np.mean(kernel_ms))
