@@ -57,8 +57,30 @@ constexpr int kCap = kWaves * kRegion;     // 8192
 constexpr int kMaxTiles = 512;
 constexpr int kList = 64;
 constexpr int kTopPTarget = 1500;          // aimed-at candidate count for top-p rows
+constexpr int kBins = 1024;                // candidate histograms: 16 bins per lane of wave 0
+constexpr int kBinsPerLane = kBins / kWave;
+constexpr int kTilesPerLane = kMaxTiles / kWave;
+static_assert(kBins == kBlock, "one bin cleared per thread");
 
 enum Mode { kArgmax = 0, kTopK = 1, kTopP = 2, kFull = 3 };
+
+// One pass of the candidate tail over every wave's region (see below).
+enum PassType : uint32_t {
+    kPassHistW = 0,   // weights of all entries, then the key histogram
+    kPassHist,        // key histogram of the entries in [lo, hi] kept by the restriction
+    kPassGather,      // list the entries in [lo, hi] kept by the restriction
+    kPassTieCount,    // per-tile counts of the entries with key == tie kept by the restriction
+    kPassTileMass,    // per-tile weight of the entries kept by the restriction
+    kPassDone,
+    kPassFallback,    // the kept prefix reaches below theta: finish from the row
+};
+
+struct PassDesc {
+    uint32_t type, lo, hi, sh;
+    uint32_t rkey, rlast;   // restriction cut
+    uint32_t tie;
+    uint32_t pad;
+};
 
 struct Smem {
     uint32_t ckey[kCap];
@@ -66,8 +88,14 @@ struct Smem {
     float cw[kCap];
     float tref[kMaxTiles];
     double tsum[kMaxTiles];
-    uint32_t hcnt[256];
-    double hmass[256];
+    double tacc[kMaxTiles];       // per-tile counts / weights of the candidate tail
+    uint16_t tstart[kMaxTiles];   // a tile's first slot in its wave's region
+    uint16_t tcnt[kMaxTiles];     // ... and its number of entries
+    alignas(16) uint32_t hcnt[kBins];
+    alignas(16) double hmass[kBins];
+    PassDesc pass;
+    double res_w;
+    uint32_t res_token, res_kept;
     uint64_t wbest[kWaves];
     uint32_t wcount[kWaves];
     uint32_t wu[kWaves];
@@ -278,6 +306,151 @@ __device__ __forceinline__ int w0_asc_mass(const uint32_t* cnt, const double* m,
     return static_cast<int>(readlane_u32(static_cast<uint32_t>(hit), first));
 }
 
+// -------------------------------------- wave-0 scans of the 1024-bin tail --
+// kBins bins, kBinsPerLane per lane: lane l holds bins l*kBinsPerLane + i.
+// Each scan also clears the bins it has read (the next pass starts from 0).
+
+struct BinPick {
+    int d;            // chosen bin, -1 if none
+    uint32_t cnt;     // its entry count
+    double mass;      // ... and weight
+    uint32_t above_c; // entries in the bins above it
+    double above_m;   // weight of the bins above it (plus the base, for mass picks)
+    bool reached;     // mass pick: the target was reached
+};
+
+// Per-lane sums of the lane's bins (one read), then wave scans.
+struct BinScan {
+    uint32_t total, pre;   // entries in all bins / in the bins before this lane's
+    double totalm, prem;   // ... their weight
+};
+
+__device__ __forceinline__ BinScan w0_scan_bins(const uint32_t* cnt, const double* m) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint4* c4 = reinterpret_cast<const uint4*>(cnt + kBinsPerLane * lane);
+    const double2* m2 = reinterpret_cast<const double2*>(m + kBinsPerLane * lane);
+    uint32_t s = 0;
+    double sm = 0.0;
+#pragma unroll
+    for (int i = 0; i < kBinsPerLane / 4; ++i) {
+        const uint4 v = c4[i];
+        s += v.x + v.y + v.z + v.w;
+    }
+#pragma unroll
+    for (int i = 0; i < kBinsPerLane / 2; ++i) {
+        const double2 v = m2[i];
+        sm += v.x;
+        sm += v.y;
+    }
+    const uint32_t incl = wave_scan_u32_dpp(s);
+    const double inclm = wave_scan_f64_dpp(sm);
+    return BinScan{readlane_u32(incl, kWave - 1), incl - s, readlane_f64(inclm, kWave - 1), inclm - sm};
+}
+
+__device__ __forceinline__ void w0_clear_bins(uint32_t* cnt, double* m) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint4* c4 = reinterpret_cast<uint4*>(cnt + kBinsPerLane * lane);
+    double2* m2 = reinterpret_cast<double2*>(m + kBinsPerLane * lane);
+#pragma unroll
+    for (int i = 0; i < kBinsPerLane / 4; ++i) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < kBinsPerLane / 2; ++i) m2[i] = make_double2(0.0, 0.0);
+}
+
+__device__ __forceinline__ BinPick w0_broadcast_pick(int hit_bin, uint32_t hcnt, double hmass, uint32_t hc,
+                                                     double hm, int src) {
+    BinPick out;
+    out.d = static_cast<int>(readlane_u32(static_cast<uint32_t>(hit_bin), src));
+    out.cnt = readlane_u32(hcnt, src);
+    out.mass = readlane_f64(hmass, src);
+    out.above_c = readlane_u32(hc, src);
+    out.above_m = readlane_f64(hm, src);
+    out.reached = true;
+    return out;
+}
+
+// The bin holding the r-th entry in descending key order (r >= 1).
+__device__ __forceinline__ BinPick w0_pick_count(uint32_t* cnt, double* m, uint32_t r) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const BinScan bs = w0_scan_bins(cnt, m);
+    uint32_t pre = bs.pre;
+    double prem = bs.prem;
+    int hit = -1;
+    uint32_t hc = 0, hcnt = 0;
+    double hm = 0.0, hmass = 0.0;
+    const uint32_t* cl = cnt + kBinsPerLane * lane;
+    const double* ml = m + kBinsPerLane * lane;
+    for (int i = 0; i < kBinsPerLane; ++i) {
+        const uint32_t b = cl[i];
+        const double bm = ml[i];
+        if (b != 0u && bs.total - pre >= r) {
+            hit = kBinsPerLane * lane + i;
+            hc = bs.total - pre - b;
+            hm = bs.totalm - prem - bm;
+            hcnt = b;
+            hmass = bm;
+        }
+        pre += b;
+        prem += bm;
+    }
+    w0_clear_bins(cnt, m);
+    const uint64_t bal = __ballot(hit >= 0);
+    if (!bal) return BinPick{-1, 0u, 0.0, 0u, 0.0, false};
+    return w0_broadcast_pick(hit, hcnt, hmass, hc, hm, 63 - __clzll(static_cast<long long>(bal)));
+}
+
+// The bin where base + the descending-order weight first reaches target:
+// the largest non-empty d with base + sum_{d' >= d} m[d'] >= target.  If no
+// bin reaches it, the lowest non-empty bin with reached = false.
+__device__ __forceinline__ BinPick w0_pick_mass(uint32_t* cnt, double* m, double base, double target) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const BinScan bs = w0_scan_bins(cnt, m);
+    uint32_t pre = bs.pre;
+    double prem = bs.prem;
+    int hit = -1, low = -1;
+    uint32_t hc = 0, hcnt = 0, lc = 0, lcnt = 0;
+    double hm = 0.0, hmass = 0.0, lm = 0.0, lmass = 0.0;
+    const uint32_t* cl = cnt + kBinsPerLane * lane;
+    const double* ml = m + kBinsPerLane * lane;
+    for (int i = 0; i < kBinsPerLane; ++i) {
+        const uint32_t b = cl[i];
+        const double bm = ml[i];
+        if (b != 0u) {
+            const uint32_t ac = bs.total - pre - b;
+            const double am = base + (bs.totalm - prem - bm);
+            if (base + (bs.totalm - prem) >= target) {
+                hit = kBinsPerLane * lane + i; hc = ac; hm = am; hcnt = b; hmass = bm;
+            }
+            if (low < 0) {
+                low = kBinsPerLane * lane + i; lc = ac; lm = am; lcnt = b; lmass = bm;
+            }
+        }
+        pre += b;
+        prem += bm;
+    }
+    w0_clear_bins(cnt, m);
+    const uint64_t bal = __ballot(hit >= 0);
+    if (bal) return w0_broadcast_pick(hit, hcnt, hmass, hc, hm, 63 - __clzll(static_cast<long long>(bal)));
+    const uint64_t nz = __ballot(low >= 0);
+    if (!nz) return BinPick{-1, 0u, 0.0, 0u, 0.0, false};
+    BinPick out = w0_broadcast_pick(low, lcnt, lmass, lc, lm, __ffsll(static_cast<unsigned long long>(nz)) - 1);
+    out.reached = false;
+    return out;
+}
+
+// Smallest shift with (range >> shift) < kBins.
+__device__ __forceinline__ int range_shift_bins(uint32_t range) {
+    return range >= static_cast<uint32_t>(kBins) ? (32 - __clz(static_cast<int>(range))) - 10 : 0;
+}
+
+// Orders the LDS accesses of one wave (the wave's lanes read what other lanes
+// of the same wave wrote).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // ------------------------------------------------------------------ kernel --
 
 template <int DT>
@@ -290,10 +463,13 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     const int b = blockIdx.x;
     const int V = a.V;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wid = threadIdx.x / kWave;
+    const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);  // wave-uniform
     const void* row = static_cast<const S*>(a.logits) + static_cast<int64_t>(b) * a.row_stride;
     const RowParams prm = row_params(a.temperature, a.top_k, a.top_p, b, V);
-    const uint64_t word = request_word(a.seed, ld_global<int64_t>(a.uid + b), a.step);
+    // The Philox word is wave-uniform scalar work (ten 64-bit multiply rounds);
+    // only wave 0 uses it, so only wave 0 pays for it on the CU's scalar unit.
+    uint64_t word = 0;
+    if (wid == 0) word = request_word(a.seed, ld_global<int64_t>(a.uid + b), a.step);
     const double u = uniform24(word);
     const int n_tiles = (V + IO::TILE - 1) / IO::TILE;
 
@@ -304,7 +480,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     else mode = kFull;
     const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
     // rows one read cannot serve go straight to the re-reading path
-    bool use_row = !aligned || ((mode == kTopP || mode == kFull) && n_tiles > kMaxTiles);
+    bool use_row = !aligned || (mode != kArgmax && n_tiles > kMaxTiles);
     const bool want_z = !use_row && (mode == kTopP || mode == kFull);
     const bool want_cand = !use_row && (mode == kTopK || mode == kTopP);
     const double c = 1.4426950408889634 / static_cast<double>(prm.T);
@@ -343,25 +519,56 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             }
         }
         if (want_cand && __ballot(tmax >= theta) != 0) {
-            // lane masks, one DPP prefix scan for the slots, predicated writes
-            uint32_t mask = 0;
+            // Slots in token order: the tile's index order is (load u, lane,
+            // element), so each load gets its own prefix over the lanes.  The
+            // per-load counts travel packed, 16 bits each, two per DPP scan.
+            uint32_t mk[IO::U];
 #pragma unroll
-            for (int q = 0; q < Q; ++q) mask |= IO::get(raw, q) >= theta ? (1u << q) : 0u;
-            const uint32_t mine = static_cast<uint32_t>(__popc(mask));
-            const uint32_t incl = wave_scan_u32_dpp(mine);
-            const uint32_t tot = readlane_u32(incl, kWave - 1);
-            if (cnt + tot <= static_cast<uint32_t>(kRegion)) {
-                uint32_t pos = static_cast<uint32_t>(wid * kRegion) + cnt + incl - mine;
+            for (int uu = 0; uu < IO::U; ++uu) {
+                mk[uu] = 0u;
 #pragma unroll
-                for (int q = 0; q < Q; ++q) {
-                    if (mask & (1u << q)) {
-                        ss.ckey[pos] = f32_key(IO::get(raw, q));
-                        ss.cidx[pos] = IO::index(t, lane, q);
-                        ++pos;
-                    }
+                for (int e = 0; e < IO::VEC; ++e)
+                    mk[uu] |= IO::get(raw, uu * IO::VEC + e) >= theta ? (1u << e) : 0u;
+            }
+            uint32_t base[IO::U], excl[IO::U];
+            uint32_t total = 0;
+#pragma unroll
+            for (int h = 0; h < (IO::U + 1) / 2; ++h) {
+                const uint32_t c0 = static_cast<uint32_t>(__popc(mk[2 * h]));
+                const uint32_t c1 = 2 * h + 1 < IO::U ? static_cast<uint32_t>(__popc(mk[2 * h + 1])) : 0u;
+                const uint32_t packed = c0 | (c1 << 16);
+                const uint32_t incl = wave_scan_u32_dpp(packed);
+                const uint32_t tot = readlane_u32(incl, kWave - 1);
+                const uint32_t ex = incl - packed;
+                base[2 * h] = total;
+                excl[2 * h] = ex & 0xffffu;
+                total += tot & 0xffffu;
+                if (2 * h + 1 < IO::U) {
+                    base[2 * h + 1] = total;
+                    excl[2 * h + 1] = ex >> 16;
+                    total += tot >> 16;
                 }
             }
-            cnt += tot;
+            if (cnt + total <= static_cast<uint32_t>(kRegion)) {
+                const uint32_t rb = static_cast<uint32_t>(wid * kRegion) + cnt;
+#pragma unroll
+                for (int uu = 0; uu < IO::U; ++uu) {
+                    uint32_t pos = rb + base[uu] + excl[uu];
+#pragma unroll
+                    for (int e = 0; e < IO::VEC; ++e) {
+                        if (mk[uu] & (1u << e)) {
+                            ss.ckey[pos] = f32_key(IO::get(raw, uu * IO::VEC + e));
+                            ss.cidx[pos] = IO::index(t, lane, uu * IO::VEC + e);
+                            ++pos;
+                        }
+                    }
+                }
+                if (lane == 0) {
+                    ss.tstart[t] = static_cast<uint16_t>(cnt);
+                    ss.tcnt[t] = static_cast<uint16_t>(total);
+                }
+            }
+            cnt += total;
         }
     };
 
@@ -372,6 +579,10 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         if (t + kWaves < n_tiles) IO::load(row, V, t + kWaves, lane, nxt);
     }
     if (want_cand) {
+        if (threadIdx.x < kMaxTiles) {
+            ss.tacc[threadIdx.x] = 0.0;
+            ss.tcnt[threadIdx.x] = 0;
+        }
         // theta: lower edge of the histogram bin holding the j-th largest of
         // the per-thread maxima of the first tiles
         float lmax = -INFINITY;
@@ -420,6 +631,10 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         } else {
             theta = -INFINITY;
         }
+        // the candidate tail's histogram starts empty (ordered before its
+        // first use by the barrier after the stream)
+        ss.hcnt[threadIdx.x] = 0u;
+        ss.hmass[threadIdx.x] = 0.0;
     }
     if (!use_row) {
         if (t < n_tiles) process(raw, t);
@@ -829,43 +1044,321 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     }
     const double Z = want_z ? ss.bd[0] : 0.0;
 
-    // ------------------------------------------------- candidate weights --
-    if (want_cand) {
-        if (overflow || (mode == kTopK && n_total < static_cast<uint32_t>(prm.k)))
-            use_row = true;
-        else {
-            const int rbase = wid * kRegion;
-            for (uint32_t i = lane; i < cnt && i < kRegion; i += kWave)
-                ss.cw[rbase + i] = static_cast<float>(fast_weight(key_f32(ss.ckey[rbase + i]), mc, c));
-        }
-    }
-
-    // ------------------------------------------ top-k, then top-p, cuts --
     Cut cut{0u, 0xffffffffu};
-    for (int pass = 0; pass < 2; ++pass) {
-        from_row = use_row;
-        cut = Cut{0u, 0xffffffffu};
-        if (mode == kTopK) cut = select_desc(cut, static_cast<uint32_t>(prm.k));
-        if (!prm.top_p) break;
-        const double wk = (mode == kTopK || use_row) ? sum_cut(cut, nullptr) : Z;
-        Cut pc;
-        const bool found = mass_cut(cut, static_cast<double>(prm.p) * wk, &pc);
-        if (found) {
-            cut = pc;
-            break;
+    uint32_t n_kept = 0, token = 0;
+    double W = 0.0;
+    bool fast = false;
+
+    // ------------------------------------------------------ candidate tail --
+    // Passes over the candidates in the wave regions; after each pass wave 0
+    // reads what the pass left (a 1024-bin key histogram, a list of at most
+    // kList entries, per-tile counts or weights) and picks the next pass.
+    //   top-k: the bin holding the k-th entry; a bin that is kept whole ends
+    //     the search, a small bin is listed and ranked exactly, a bin of one
+    //     key (a run of ties) is resolved in token order by per-tile counts,
+    //     a larger bin is histogrammed again over its own key range;
+    //   top-p: the same descent by weight, inside the top-k cut;
+    //   the draw: per-tile kept weight, a scan over the tiles, then a scan of
+    //     the one tile's entries in slot order, which is token order.
+    if (want_cand) {
+        if (overflow || (mode == kTopK && n_total < static_cast<uint32_t>(prm.k))) {
+            use_row = true;
+        } else {
+            constexpr int kTileShift = __builtin_ctz(IO::TILE);
+            const uint32_t key_hi = f32_key(m);
+            // wave-0 state (the other waves keep unused copies)
+            int phase = mode == kTopK ? 0 : 1;      // 0 top-k, 1 top-p, 2 the draw
+            bool first_p = mode == kTopP;
+            uint32_t lo = f32_key(theta), hi = key_hi;
+            uint32_t sh = static_cast<uint32_t>(range_shift_bins(hi - lo));
+            uint32_t r = static_cast<uint32_t>(prm.k);
+            uint32_t above_c = 0, nk = 0, tie = 0, tie_r = 0;
+            double above_m = 0.0, wk = 0.0;
+            double target = static_cast<double>(prm.p) * Z;
+            Cut rc{0u, 0xffffffffu}, res{0u, 0xffffffffu};
+
+            auto mk = [&](uint32_t type) {
+                PassDesc x;
+                x.type = type; x.lo = lo; x.hi = hi; x.sh = sh;
+                x.rkey = rc.key; x.rlast = rc.last; x.tie = tie; x.pad = 0u;
+                return x;
+            };
+            auto tie_weight = [&](uint32_t k) {
+                return static_cast<double>(static_cast<float>(fast_weight(key_f32(k), mc, c)));
+            };
+
+            auto run_pass = [&](const PassDesc& pd) {
+                const int rbase = wid * kRegion;
+                const uint32_t n = cnt < static_cast<uint32_t>(kRegion) ? cnt : static_cast<uint32_t>(kRegion);
+                const Cut rcut{pd.rkey, pd.rlast};
+                for (uint32_t i = lane; i < n; i += kWave) {
+                    const int sl = rbase + static_cast<int>(i);
+                    const uint32_t key = ss.ckey[sl];
+                    if (pd.type == kPassHistW) {
+                        const float w = static_cast<float>(fast_weight(key_f32(key), mc, c));
+                        ss.cw[sl] = w;
+                        const uint32_t d = (key - pd.lo) >> pd.sh;
+                        atomicAdd(&ss.hcnt[d], 1u);
+                        atomicAdd(&ss.hmass[d], static_cast<double>(w));
+                        continue;
+                    }
+                    if (pd.type == kPassHist || pd.type == kPassGather) {
+                        if (key < pd.lo || key > pd.hi) continue;
+                    } else if (pd.type == kPassTieCount) {
+                        if (key != pd.tie) continue;
+                    }
+                    const uint32_t idx = ss.cidx[sl];
+                    if (!rcut.keep(idx, key)) continue;
+                    if (pd.type == kPassHist) {
+                        const uint32_t d = (key - pd.lo) >> pd.sh;
+                        atomicAdd(&ss.hcnt[d], 1u);
+                        atomicAdd(&ss.hmass[d], static_cast<double>(ss.cw[sl]));
+                    } else if (pd.type == kPassGather) {
+                        const uint32_t p = atomicAdd(&ss.list_n, 1u);
+                        if (p < static_cast<uint32_t>(kList)) {
+                            ss.lkey[p] = key;
+                            ss.lidx[p] = idx;
+                            ss.lw[p] = ss.cw[sl];
+                        }
+                    } else if (pd.type == kPassTieCount) {
+                        atomicAdd(&ss.tacc[idx >> kTileShift], 1.0);
+                    } else {
+                        atomicAdd(&ss.tacc[idx >> kTileShift], static_cast<double>(ss.cw[sl]));
+                    }
+                }
+            };
+
+            // wave 0: the entry selected by per-tile counts (the want-th, 1-based,
+            // in token order) or weights (first whose prefix exceeds want * total)
+            auto tile_select = [&](bool by_mass, double want, double* total_out) -> uint32_t {
+                double* tl = ss.tacc + lane * kTilesPerLane;   // zero past n_tiles
+                double v[kTilesPerLane];
+                double sl = 0.0;
+#pragma unroll
+                for (int i = 0; i < kTilesPerLane; ++i) {
+                    v[i] = tl[i];
+                    sl += v[i];
+                }
+#pragma unroll
+                for (int i = 0; i < kTilesPerLane; ++i) tl[i] = 0.0;
+                const double incl = wave_scan_f64_dpp(sl);
+                const double total = readlane_f64(incl, kWave - 1);
+                const double tgt = by_mass ? want * total : want;
+                *total_out = total;
+                const uint64_t hb = __ballot(sl > 0.0 && (by_mass ? incl > tgt : incl >= tgt));
+                const uint64_t nzb = __ballot(sl > 0.0);
+                if (!nzb) return 0u;
+                const int owner = hb ? __ffsll(static_cast<unsigned long long>(hb)) - 1
+                                     : 63 - __clzll(static_cast<long long>(nzb));
+                int ts = -1, last_nz = -1;
+                double rem = 0.0;
+                if (lane == owner) {
+                    double cum = incl - sl;
+#pragma unroll
+                    for (int i = 0; i < kTilesPerLane; ++i) {
+                        if (ts < 0 && v[i] > 0.0) {
+                            last_nz = lane * kTilesPerLane + i;
+                            if (hb && (by_mass ? cum + v[i] > tgt : cum + v[i] >= tgt)) {
+                                ts = last_nz;
+                                rem = tgt - cum;
+                            } else {
+                                cum += v[i];
+                            }
+                        }
+                    }
+                    if (ts < 0) {            // rounding: take the last entry
+                        ts = last_nz;
+                        rem = INFINITY;
+                    }
+                }
+                ts = static_cast<int>(readlane_u32(static_cast<uint32_t>(ts), owner));
+                rem = readlane_f64(rem, owner);
+                const int sb = (ts & (kWaves - 1)) * kRegion + ss.tstart[ts];
+                const int n = ss.tcnt[ts];
+                const Cut rcut = rc;
+                double run = 0.0;
+                uint32_t found = 0xffffffffu, last = 0xffffffffu;
+                for (int j0 = 0; j0 < n; j0 += kWave) {
+                    const int j = j0 + lane;
+                    bool pr = false;
+                    double val = 0.0;
+                    uint32_t idx = 0;
+                    if (j < n) {
+                        const uint32_t k2 = ss.ckey[sb + j];
+                        idx = ss.cidx[sb + j];
+                        pr = rcut.keep(idx, k2) && (by_mass || k2 == tie);
+                        val = pr ? (by_mass ? static_cast<double>(ss.cw[sb + j]) : 1.0) : 0.0;
+                    }
+                    const double in2 = wave_scan_f64_dpp(val);
+                    const uint64_t hit = __ballot(val > 0.0 && (by_mass ? run + in2 > rem : run + in2 >= rem));
+                    const uint64_t pb = __ballot(val > 0.0);
+                    if (pb) last = readlane_u32(idx, 63 - __clzll(static_cast<long long>(pb)));
+                    if (hit) {
+                        found = readlane_u32(idx, __ffsll(static_cast<unsigned long long>(hit)) - 1);
+                        break;
+                    }
+                    run += readlane_f64(in2, kWave - 1);
+                }
+                return found != 0xffffffffu ? found : last;
+            };
+
+            auto enter_next = [&]() -> PassDesc {
+                if (phase == 0 && prm.top_p) {
+                    // top-p inside the top-k cut, against its weight
+                    phase = 1;
+                    rc = res;
+                    target = static_cast<double>(prm.p) * wk;
+                    lo = res.key;
+                    hi = key_hi;
+                    sh = static_cast<uint32_t>(range_shift_bins(hi - lo));
+                    above_c = 0;
+                    above_m = 0.0;
+                    return mk(kPassHist);
+                }
+                phase = 2;
+                rc = res;
+                return mk(kPassTileMass);
+            };
+
+            auto step = [&](uint32_t done_type) -> PassDesc {
+                if (done_type == kPassHistW || done_type == kPassHist) {
+                    const BinPick bp = phase == 0 ? w0_pick_count(ss.hcnt, ss.hmass, r)
+                                                  : w0_pick_mass(ss.hcnt, ss.hmass, above_m, target);
+                    if (bp.d < 0 || (first_p && !bp.reached)) return mk(kPassFallback);
+                    first_p = false;
+                    above_c += bp.above_c;
+                    if (phase == 0) {
+                        above_m += bp.above_m;
+                        r -= bp.above_c;
+                    } else {
+                        above_m = bp.above_m;
+                    }
+                    const uint32_t blo = lo + (static_cast<uint32_t>(bp.d) << sh);
+                    const uint32_t bhi = bin_hi(blo, static_cast<int>(sh), hi);
+                    if (phase == 0 && r == bp.cnt) {        // the bin is kept whole
+                        res = Cut{blo, 0xffffffffu};
+                        wk = above_m + bp.mass;
+                        nk = above_c + bp.cnt;
+                        return enter_next();
+                    }
+                    lo = blo;
+                    hi = bhi;
+                    if (bp.cnt <= static_cast<uint32_t>(kList)) return mk(kPassGather);
+                    if (blo == bhi) {                       // a run of equal keys
+                        tie = blo;
+                        if (phase == 0) {
+                            tie_r = r;
+                            return mk(kPassTieCount);
+                        }
+                        // each weighs w: the j-th (token order) has exclusive prefix above + (j-1) w
+                        const double w = tie_weight(blo);
+                        uint32_t keep = bp.cnt;
+                        if (bp.reached) {
+                            const double y = (target - above_m) / w;
+                            if (y < static_cast<double>(bp.cnt)) {
+                                const double cy = ceil(y);
+                                keep = cy < 1.0 ? 1u : static_cast<uint32_t>(cy);
+                            }
+                        }
+                        if (keep == bp.cnt) {
+                            res = rc.key == blo ? rc : Cut{blo, 0xffffffffu};
+                            nk = above_c + bp.cnt;
+                            return enter_next();
+                        }
+                        tie_r = keep;
+                        return mk(kPassTieCount);
+                    }
+                    sh = static_cast<uint32_t>(range_shift_bins(hi - lo));
+                    return mk(kPassHist);
+                }
+                if (done_type == kPassGather) {
+                    const int n = ss.list_n < static_cast<uint32_t>(kList) ? static_cast<int>(ss.list_n) : kList;
+                    if (lane < n) {
+                        const uint32_t k = ss.lkey[lane], i = ss.lidx[lane];
+                        int rr = 0;
+                        for (int e = 0; e < n; ++e) {
+                            const uint32_t k2 = ss.lkey[e], i2 = ss.lidx[e];
+                            rr += (k2 > k || (k2 == k && i2 < i)) ? 1 : 0;
+                        }
+                        ss.skey[rr] = k;
+                        ss.sidx[rr] = i;
+                        ss.sw[rr] = ss.lw[lane];
+                    }
+                    wave_lds_sync();
+                    if (lane == 0) ss.list_n = 0u;
+                    const bool in = lane < n;
+                    const uint32_t kk = in ? ss.skey[lane] : 0u, ii = in ? ss.sidx[lane] : 0u;
+                    const double w = in ? static_cast<double>(ss.sw[lane]) : 0.0;
+                    const double incl = wave_scan_f64_dpp(w);
+                    int e;
+                    if (phase == 0) {
+                        e = static_cast<int>(r) - 1;
+                        wk = above_m + readlane_f64(incl, e);
+                    } else {
+                        const uint64_t bal = __ballot(in && above_m + incl >= target);
+                        e = bal ? __ffsll(static_cast<unsigned long long>(bal)) - 1 : n - 1;
+                    }
+                    res = Cut{readlane_u32(kk, e), readlane_u32(ii, e)};
+                    nk = above_c + static_cast<uint32_t>(e) + 1u;
+                    return enter_next();
+                }
+                if (done_type == kPassTieCount) {
+                    double unused;
+                    const uint32_t idx = tile_select(false, static_cast<double>(tie_r), &unused);
+                    res = Cut{tie, idx};
+                    if (phase == 0) wk = above_m + static_cast<double>(tie_r) * tie_weight(tie);
+                    nk = above_c + tie_r;
+                    return enter_next();
+                }
+                // the draw
+                double total = 0.0;
+                const uint32_t tok = tile_select(true, u, &total);
+                if (lane == 0) {
+                    ss.res_token = tok;
+                    ss.res_kept = nk;
+                    ss.res_w = total;
+                }
+                return mk(kPassDone);
+            };
+
+            PassDesc pd = mk(kPassHistW);
+            if (threadIdx.x == 0) ss.list_n = 0u;
+            for (;;) {
+                run_pass(pd);
+                __syncthreads();
+                if (wid == 0) {
+                    const PassDesc nx = step(pd.type);
+                    if (lane == 0) ss.pass = nx;
+                }
+                __syncthreads();
+                pd = ss.pass;
+                if (pd.type == kPassDone || pd.type == kPassFallback) break;
+            }
+            if (pd.type == kPassDone) {
+                fast = true;
+                cut = Cut{pd.rkey, pd.rlast};
+                token = ss.res_token;
+                n_kept = ss.res_kept;
+                W = ss.res_w;
+            } else {
+                use_row = true;
+            }
         }
-        // the mass never reached p * W inside the entries: top-k keeps all of
-        // its set (rounding only); top-p over candidates must see the whole row
-        if (mode == kTopK || use_row) break;
-        use_row = true;
     }
 
-    // ---- the draw: first index (token order) whose kept prefix exceeds u*W --
-    uint32_t n_kept = 0;
-    const double W = sum_cut(cut, &n_kept);
-    double tgt = u * W;
-    uint32_t token;
-    {
+    if (!fast) {
+        // ---------------------------- the row itself: top-k, then top-p --
+        from_row = true;
+        if (mode == kTopK) cut = select_desc(cut, static_cast<uint32_t>(prm.k));
+        if (prm.top_p) {
+            const double wk = sum_cut(cut, nullptr);
+            Cut pc;
+            if (mass_cut(cut, static_cast<double>(prm.p) * wk, &pc)) cut = pc;
+        }
+
+        // ---- the draw: first index (token order) whose kept prefix exceeds u*W --
+        W = sum_cut(cut, &n_kept);
+        double tgt = u * W;
         auto kept = [&](uint32_t k, uint32_t i) { return cut.keep(i, k); };
         uint32_t ilo = 0, ihi = static_cast<uint32_t>(V - 1);
         for (;;) {
