@@ -12,7 +12,9 @@
 // workgroup, and folds the result into the row's 64-bit slot with one
 // atomicMax.  The last workgroup of the row to arrive (counted with an atomic
 // ticket) reads the slot, writes the token and resets the slot and counter,
-// so the workspace is clean for the next call without a memset.
+// so the workspace is clean for the next call without a memset.  Batches of
+// at least 256 rows use the single-pass sampler kernel instead (one
+// workgroup per row already fills the GPU).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -84,23 +86,31 @@ __global__ __launch_bounds__(kArgmaxBlock) void argmax_rows_kernel(ArgmaxArgs a)
     }
     best = block_max<kArgmaxBlock>(best, red);
 
-    // debug: zero this chunk's slice of probs_out (the one-hot 1 comes last)
+    // debug: zero this chunk's slice of probs_out (the one-hot 1 comes last);
+    // the zeros must reach memory before this chunk's ticket, since the last
+    // chunk of the row may run on another XCD with its own L2
     if (a.probs_out) {
         float* pr = a.probs_out + static_cast<int64_t>(b) * a.V;
         for (int64_t t = lo + threadIdx.x; t < hi; t += kArgmaxBlock) pr[t] = 0.0f;
+        __syncthreads();
+        if (threadIdx.x == 0) __threadfence();
     }
 
     if (threadIdx.x == 0) {
         uint64_t final_best = best;
         bool last = true;
         if (a.chunks > 1) {
-            atomicMax(reinterpret_cast<unsigned long long*>(a.slot + b),
-                      static_cast<unsigned long long>(best));
-            __threadfence();
+            // Device-scope atomics are performed where every XCD sees them;
+            // consuming each returned value makes this thread wait for the
+            // atomic to complete before issuing the next one, which is the
+            // only ordering needed (no plain data is exchanged, so no L2
+            // write-back / invalidate fence).
+            const unsigned long long prev = atomicMax(reinterpret_cast<unsigned long long*>(a.slot + b),
+                                                      static_cast<unsigned long long>(best));
+            asm volatile("" ::"v"(prev));   // the returned value must have arrived
             const uint32_t arrived = atomicAdd(a.count + b, 1u);
             last = arrived == static_cast<uint32_t>(a.chunks - 1);
             if (last) {
-                __threadfence();
                 final_best = atomicExch(reinterpret_cast<unsigned long long*>(a.slot + b), 0ull);
                 atomicExch(a.count + b, 0u);
             }
@@ -133,11 +143,12 @@ hipError_t launch_argmax(const ArgmaxArgs& args, int dtype, hipStream_t stream) 
 }
 
 void argmax_plan(int B, int V, int dtype, int* chunks, int* chunk_len) {
-    // aim for >= 2048 workgroups over the batch; chunks are whole 16-byte
-    // vectors per thread-block pass so row alignment carries into every chunk
+    // aim for ~1024 workgroups over the batch (four per CU); chunks are whole
+    // 16-byte vectors per thread-block pass so row alignment carries into
+    // every chunk
     const int vec = dtype == kDtypeF32 ? 4 : 8;
     const int quantum = kArgmaxBlock * vec;
-    int want = (2048 + B - 1) / (B > 0 ? B : 1);
+    int want = (1024 + B - 1) / (B > 0 ? B : 1);
     int len = (V + want - 1) / want;
     len = ((len + quantum - 1) / quantum) * quantum;
     if (len < quantum) len = quantum;

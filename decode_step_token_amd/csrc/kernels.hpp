@@ -26,10 +26,10 @@ struct SampleArgs {
     const void* logits;
     int64_t row_stride;
     int B, V;
-    const float* temperature;  // non-null
+    const float* temperature;  // null: every row greedy
     const int32_t* top_k;      // may be null
     const float* top_p;        // may be null
-    const int64_t* uid;        // non-null
+    const int64_t* uid;        // non-null unless temperature is null
     uint64_t step, seed;
     int32_t* tokens_out;
     float* probs_out;

@@ -8,38 +8,34 @@
 // (key, last index): token i is kept iff key_i > key, or key_i == key and
 // i <= last index.
 //
-// What one read of the row leaves behind:
+// The row is read in tiles of 1024 logits (4 KB fp32, 2 KB bf16); tile t
+// belongs to wave t mod 16.  What one read leaves behind:
 //   * the row maximum and its lowest index, from per-tile lane maxima (the
 //     argmax bookkeeping only runs when a lane's tile beats its running best);
-//   * for rows without top-k: one softmax sum per tile (1024 fp32 or 2048
-//     bf16 logits) relative to the tile's own maximum tref, with fp32
-//     arguments (x - tref) * log2(e)/T through v_exp_f32, rescaled to the row
-//     maximum in fp64 at the end.  (x - tref) is exact for every logit within
-//     a factor two of tref, which carries the tile's mass, so the normaliser
-//     stays within ~2e-7 of the fp64 sum on the workloads here (an argument
-//     taken relative to the row maximum in one fp32 expression is off by up
-//     to 2.5e-6);
-//   * for rows with top-k or top-p: every logit >= theta, with its index, in a
-//     wave-private LDS region (ballot + mbcnt compaction, a scalar counter, no
-//     LDS atomics).  theta is fixed after the first tile of every wave: the
-//     lower edge of the histogram bin that holds the j-th largest of the 1024
+//   * rows without top-k or top-p: one softmax sum per tile, relative to the
+//     tile's own maximum tref, with fp32 arguments (x - tref) * log2(e)/T
+//     through v_exp_f32, rescaled to the row maximum in fp64 at the end.
+//     (x - tref) is exact for every logit within a factor two of tref, which
+//     carries the tile's mass, so the normaliser stays within ~2e-7 of the
+//     fp64 sum (an argument taken relative to the row maximum in one fp32
+//     expression is off by up to 2.5e-6);
+//   * top-p rows: the same sums per lane, against the lane's running maximum
+//     (online rescaling when it grows), accumulated in fp64;
+//   * rows with top-k or top-p: every logit >= theta, with its index, in a
+//     wave-private LDS region in token order, with each tile's first slot and
+//     count.  theta is fixed after the first tile of every wave: the lower
+//     edge of the histogram bin that holds the j-th largest of the 1024
 //     per-thread maxima.  j = k for top-k: j per-thread maxima are j distinct
 //     logits >= theta, so the top-k set is always inside the regions.  For
-//     top-p, j aims at a few thousand candidates.
+//     top-p, j aims at about 1500 candidates.
 //
-// Finishing the row: all waves build 256-bin LDS histograms of their own
-// entries; wave 0 scans them with DPP prefix sums and picks the bin; a bin of
-// at most 64 entries is gathered and ranked exactly.
-//   * full softmax (no top-k, top-p = 1): the tile sums are rescaled and
-//     scanned; the one tile holding u * Z is read again and scanned;
-//   * top-k: count descent over the keys;
-//   * top-p: mass descent over the keys inside the top-k cut;
-//   * the draw: mass descent over the token index of the kept entries.
-// The candidates are every logit >= theta, a prefix of the descending order,
-// so the result is exact whenever the kept prefix ends inside them.  When it
-// does not (a flat top-p row whose nucleus reaches below theta, a full
-// region, top-k above the thread count), or the row is not 16-byte aligned,
-// the same descents run over the row itself, re-reading it from memory.
+// Finishing the row from the candidates is a sequence of block-wide passes
+// over the regions; after each one wave 0 reads what the pass produced and
+// picks the next pass (see the candidate tail below).  Rows without top-k or
+// top-p draw from the tile sums and read one tile again.  When the kept
+// prefix does not end inside the candidates (a flat top-p row whose nucleus
+// reaches below theta, a full region), or the row is not 16-byte aligned,
+// exact block-wide descents run over the row itself, re-reading it.
 //
 // Everything is inline and spill-free: a kernel that needs scratch memory
 // pays ~10 us per launch on this GPU.
@@ -83,8 +79,7 @@ struct PassDesc {
 };
 
 struct Smem {
-    uint32_t ckey[kCap];
-    uint32_t cidx[kCap];
+    uint2 cent[kCap];             // candidates: (value bits, later the order key; token index)
     float cw[kCap];
     float tref[kMaxTiles];
     double tsum[kMaxTiles];
@@ -469,7 +464,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     // The Philox word is wave-uniform scalar work (ten 64-bit multiply rounds);
     // only wave 0 uses it, so only wave 0 pays for it on the CU's scalar unit.
     uint64_t word = 0;
-    if (wid == 0) word = request_word(a.seed, ld_global<int64_t>(a.uid + b), a.step);
+    if (wid == 0 && a.uid) word = request_word(a.seed, ld_global<int64_t>(a.uid + b), a.step);
     const double u = uniform24(word);
     const int n_tiles = (V + IO::TILE - 1) / IO::TILE;
 
@@ -481,7 +476,8 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
     // rows one read cannot serve go straight to the re-reading path
     bool use_row = !aligned || (mode != kArgmax && n_tiles > kMaxTiles);
-    const bool want_z = !use_row && (mode == kTopP || mode == kFull);
+    const bool want_tiles = !use_row && mode == kFull;    // per-tile softmax sums
+    const bool want_lanez = !use_row && mode == kTopP;    // per-lane softmax sums
     const bool want_cand = !use_row && (mode == kTopK || mode == kTopP);
     const double c = 1.4426950408889634 / static_cast<double>(prm.T);
 
@@ -491,6 +487,9 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     float theta = INFINITY;
     const float c32 = static_cast<float>(c);
     uint32_t cnt = 0;                 // this wave's region fill (wave-uniform)
+
+    float lref = -INFINITY;           // top-p rows: this lane's running reference
+    double lsum = 0.0;                // ... and its exponent sum relative to it
 
     auto process = [&](const uint4* raw, int t) {
         float tmax = IO::get(raw, 0);
@@ -504,7 +503,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             best_t = t;
             best_q = qq;
         }
-        if (want_z) {
+        if (want_tiles) {
             // tile-local reference: (x - tref) is exact for the logits that
             // carry the tile's mass, so fp32 arguments are accurate here; the
             // tile sum is rescaled to the row maximum in fp64 at the end
@@ -518,50 +517,57 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 ss.tsum[t] = st;
             }
         }
+        if (want_lanez) {
+            // the same argument per lane, against the lane's running maximum
+            // (online rescaling when it grows), accumulated in fp64
+            if (tmax > lref) {
+                if (lsum > 0.0) lsum *= exp2_neg((static_cast<double>(lref) - static_cast<double>(tmax)) * c);
+                lref = tmax;
+            }
+            float s = 0.0f;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) s += __builtin_amdgcn_exp2f((IO::get(raw, q) - lref) * c32);
+            lsum += static_cast<double>(s);
+        }
         if (want_cand && __ballot(tmax >= theta) != 0) {
             // Slots in token order: the tile's index order is (load u, lane,
-            // element), so each load gets its own prefix over the lanes.  The
-            // per-load counts travel packed, 16 bits each, two per DPP scan.
-            uint32_t mk[IO::U];
+            // element), so each load needs its own prefix over the lanes.  The
+            // per-load counts travel packed in one DPP scan (8-bit fields for
+            // four loads: an exclusive prefix is at most 63 * 4; 16-bit fields
+            // for two).  The values are stored as raw bits; the tail turns
+            // them into order keys.
+            constexpr int FB = 32 / IO::U;
+            constexpr uint32_t FM = (1u << FB) - 1u;
+            uint32_t packed = 0;
 #pragma unroll
             for (int uu = 0; uu < IO::U; ++uu) {
-                mk[uu] = 0u;
+                uint32_t cu = 0;
 #pragma unroll
-                for (int e = 0; e < IO::VEC; ++e)
-                    mk[uu] |= IO::get(raw, uu * IO::VEC + e) >= theta ? (1u << e) : 0u;
+                for (int e = 0; e < IO::VEC; ++e) cu += IO::get(raw, uu * IO::VEC + e) >= theta ? 1u : 0u;
+                packed |= cu << (FB * uu);
             }
-            uint32_t base[IO::U], excl[IO::U];
+            const uint32_t ex = wave_scan_u32_dpp(packed) - packed;
+            const uint32_t ex_last = readlane_u32(ex, kWave - 1);
+            const uint32_t pk_last = readlane_u32(packed, kWave - 1);
             uint32_t total = 0;
 #pragma unroll
-            for (int h = 0; h < (IO::U + 1) / 2; ++h) {
-                const uint32_t c0 = static_cast<uint32_t>(__popc(mk[2 * h]));
-                const uint32_t c1 = 2 * h + 1 < IO::U ? static_cast<uint32_t>(__popc(mk[2 * h + 1])) : 0u;
-                const uint32_t packed = c0 | (c1 << 16);
-                const uint32_t incl = wave_scan_u32_dpp(packed);
-                const uint32_t tot = readlane_u32(incl, kWave - 1);
-                const uint32_t ex = incl - packed;
-                base[2 * h] = total;
-                excl[2 * h] = ex & 0xffffu;
-                total += tot & 0xffffu;
-                if (2 * h + 1 < IO::U) {
-                    base[2 * h + 1] = total;
-                    excl[2 * h + 1] = ex >> 16;
-                    total += tot >> 16;
-                }
-            }
+            for (int uu = 0; uu < IO::U; ++uu)
+                total += ((ex_last >> (FB * uu)) & FM) + ((pk_last >> (FB * uu)) & FM);
             if (cnt + total <= static_cast<uint32_t>(kRegion)) {
-                const uint32_t rb = static_cast<uint32_t>(wid * kRegion) + cnt;
+                const uint32_t lanebase = IO::index(t, lane, 0);
+                uint32_t base = static_cast<uint32_t>(wid * kRegion) + cnt;
 #pragma unroll
                 for (int uu = 0; uu < IO::U; ++uu) {
-                    uint32_t pos = rb + base[uu] + excl[uu];
+                    uint32_t pos = base + ((ex >> (FB * uu)) & FM);
 #pragma unroll
                     for (int e = 0; e < IO::VEC; ++e) {
-                        if (mk[uu] & (1u << e)) {
-                            ss.ckey[pos] = f32_key(IO::get(raw, uu * IO::VEC + e));
-                            ss.cidx[pos] = IO::index(t, lane, uu * IO::VEC + e);
+                        const float x = IO::get(raw, uu * IO::VEC + e);
+                        if (x >= theta) {
+                            ss.cent[pos] = make_uint2(__float_as_uint(x), lanebase + uu * kWave * IO::VEC + e);
                             ++pos;
                         }
                     }
+                    base += ((ex_last >> (FB * uu)) & FM) + ((pk_last >> (FB * uu)) & FM);
                 }
                 if (lane == 0) {
                     ss.tstart[t] = static_cast<uint16_t>(cnt);
@@ -706,8 +712,8 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             const int rbase = wid * kRegion;
             const uint32_t n = cnt < kRegion ? cnt : kRegion;
             for (uint32_t i = lane; i < n; i += kWave) {
-                const uint32_t idx = ss.cidx[rbase + i];
-                if (idx >= ilo && idx <= ihi) f(ss.ckey[rbase + i], idx, static_cast<int>(rbase + i));
+                const uint2 en = ss.cent[rbase + i];
+                if (en.y >= ilo && en.y <= ihi) f(en.x, en.y, static_cast<int>(rbase + i));
             }
         } else {
             const uint32_t hi = ihi < static_cast<uint32_t>(V - 1) ? ihi : static_cast<uint32_t>(V - 1);
@@ -939,8 +945,8 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         }
     };
 
-    // ------------------------------------------------- softmax normaliser --
-    if (want_z) {
+    // ------------------- rows without top-k or top-p: draw from tile sums --
+    if (want_tiles) {
         if (wid == 0) {
             const int per = (n_tiles + kWave - 1) / kWave;
             const int tlo = lane * per, thi = tlo + per < n_tiles ? tlo + per : n_tiles;
@@ -1042,7 +1048,14 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             return;
         }
     }
-    const double Z = want_z ? ss.bd[0] : 0.0;
+    // top-p rows: the per-lane sums rescaled to the row maximum; wave 0 adds
+    // the wave partials once the next barrier has passed
+    if (want_lanez) {
+        const double part = lsum > 0.0
+            ? lsum * exp2_neg((static_cast<double>(lref) - static_cast<double>(m)) * c) : 0.0;
+        const double ws = wave_sum_dpp(part);
+        if (lane == 0) ss.wd[wid] = ws;
+    }
 
     Cut cut{0u, 0xffffffffu};
     uint32_t n_kept = 0, token = 0;
@@ -1074,7 +1087,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             uint32_t r = static_cast<uint32_t>(prm.k);
             uint32_t above_c = 0, nk = 0, tie = 0, tie_r = 0;
             double above_m = 0.0, wk = 0.0;
-            double target = static_cast<double>(prm.p) * Z;
+            double target = 0.0;
             Cut rc{0u, 0xffffffffu}, res{0u, 0xffffffffu};
 
             auto mk = [&](uint32_t type) {
@@ -1093,21 +1106,25 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 const Cut rcut{pd.rkey, pd.rlast};
                 for (uint32_t i = lane; i < n; i += kWave) {
                     const int sl = rbase + static_cast<int>(i);
-                    const uint32_t key = ss.ckey[sl];
                     if (pd.type == kPassHistW) {
-                        const float w = static_cast<float>(fast_weight(key_f32(key), mc, c));
+                        // the stream stored raw value bits: turn them into order keys
+                        const float x = __uint_as_float(ss.cent[sl].x);
+                        const uint32_t key = f32_key(x);
+                        ss.cent[sl].x = key;
+                        const float w = static_cast<float>(fast_weight(x, mc, c));
                         ss.cw[sl] = w;
                         const uint32_t d = (key - pd.lo) >> pd.sh;
                         atomicAdd(&ss.hcnt[d], 1u);
                         atomicAdd(&ss.hmass[d], static_cast<double>(w));
                         continue;
                     }
+                    const uint32_t key = ss.cent[sl].x;
                     if (pd.type == kPassHist || pd.type == kPassGather) {
                         if (key < pd.lo || key > pd.hi) continue;
                     } else if (pd.type == kPassTieCount) {
                         if (key != pd.tie) continue;
                     }
-                    const uint32_t idx = ss.cidx[sl];
+                    const uint32_t idx = ss.cent[sl].y;
                     if (!rcut.keep(idx, key)) continue;
                     if (pd.type == kPassHist) {
                         const uint32_t d = (key - pd.lo) >> pd.sh;
@@ -1184,8 +1201,9 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                     double val = 0.0;
                     uint32_t idx = 0;
                     if (j < n) {
-                        const uint32_t k2 = ss.ckey[sb + j];
-                        idx = ss.cidx[sb + j];
+                        const uint2 en = ss.cent[sb + j];
+                        const uint32_t k2 = en.x;
+                        idx = en.y;
                         pr = rcut.keep(idx, k2) && (by_mass || k2 == tie);
                         val = pr ? (by_mass ? static_cast<double>(ss.cw[sb + j]) : 1.0) : 0.0;
                     }
@@ -1221,6 +1239,13 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             };
 
             auto step = [&](uint32_t done_type) -> PassDesc {
+                if (first_p) {
+                    // the softmax normaliser of a top-p row
+                    double z = 0.0;
+#pragma unroll
+                    for (int w = 0; w < kWaves; ++w) z += ss.wd[w];
+                    target = static_cast<double>(prm.p) * z;
+                }
                 if (done_type == kPassHistW || done_type == kPassHist) {
                     const BinPick bp = phase == 0 ? w0_pick_count(ss.hcnt, ss.hmass, r)
                                                   : w0_pick_mass(ss.hcnt, ss.hmass, above_m, target);

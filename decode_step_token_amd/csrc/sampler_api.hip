@@ -19,6 +19,9 @@
 namespace {
 
 constexpr int kRing = 256;
+// all-greedy batches with at least this many rows fill the GPU with one
+// workgroup per row and take the single-pass kernel; smaller ones split rows
+constexpr int kStreamGreedyMinRows = 256;
 
 struct DeviceGuard {
     int prev = -1;
@@ -155,7 +158,7 @@ int sample_batch(dst_sampler* s, void* stream, const void* logits, int64_t row_s
     DeviceGuard g(s->device);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (!temperature) {
+    if (!temperature && B < kStreamGreedyMinRows) {
         dst::ArgmaxArgs a{};
         a.logits = logits;
         a.row_stride = row_stride;

@@ -95,6 +95,28 @@ def test_greedy_batch_without_temperature_bf16():
     _check(w)
 
 
+@pytest.mark.parametrize("B,V,dtype", [(256, 5000, "bf16"), (300, 20000, "f32"), (255, 3001, "f32")])
+def test_all_greedy_batches_both_kernels(B, V, dtype):
+    """No temperature array: batches below 256 rows split rows across
+    workgroups, larger ones take one workgroup per row; both must give the
+    lowest-index maximum, including injected ties."""
+    rng = np.random.default_rng(B * 31 + V)
+    w = wl.tiny(rng, B, V, dtype)
+    w.temperature = None
+    for b in range(0, B, 7):            # exact ties with the row maximum
+        i = int(np.argmax(w.logits[b]))
+        j = int(rng.integers(0, V))
+        w.logits[b, j] = w.logits[b, i]
+    gpu, _ = _check(w)
+    want = np.argmax(oracle_widen(w), axis=1)
+    assert np.array_equal(gpu["tokens"], want)
+
+
+def oracle_widen(w):
+    import oracle
+    return oracle.widen_logits(w.logits, w.dtype)
+
+
 @pytest.mark.parametrize("V,dtype", [(1000, "f32"), (5000, "bf16"), (33000, "f32")])
 def test_tiny_mixed_batches_exact_path(V, dtype):
     w = wl.tiny(np.random.default_rng(V * 11), 48, V, dtype)
