@@ -78,6 +78,16 @@ struct PassDesc {
     uint32_t pad;
 };
 
+// A bin picked by the block-parallel histogram scan.
+struct BlockPick {
+    int d;              // bin, -1 if the mass target is not reached
+    uint32_t cnt;       // entries in the bin
+    uint32_t above_c;   // entries in the bins above it
+    uint32_t pad;
+    double mass;        // weight of the bin
+    double above_m;     // weight of the bins above it
+};
+
 struct Smem {
     uint2 cent[kCap];             // candidates: (value bits, later the order key; token index)
     float cw[kCap];
@@ -89,6 +99,7 @@ struct Smem {
     alignas(16) uint32_t hcnt[kBins];
     alignas(16) double hmass[kBins];
     PassDesc pass;
+    uint64_t word;                // the row's Philox word (written by wave 0)
     double res_w;
     uint32_t res_token, res_kept;
     uint64_t wbest[kWaves];
@@ -104,6 +115,16 @@ struct Smem {
     uint32_t skey[kList];  // ... ranked
     uint32_t sidx[kList];
     float sw[kList];
+    // block-parallel picks and ranks
+    uint32_t wtc[kWaves];  // per-wave totals of a pick or tile scan
+    double wtm[kWaves];
+    BlockPick pick;
+    uint32_t rankp[kList]; // rank of list entry i in descending order / in token order
+    uint32_t ranki[kList];
+    uint32_t xrp[kList];   // list in token order: its descending rank, weight, index
+    float xw[kList];
+    uint32_t xidx[kList];
+    uint32_t cut_key, cut_last;
 };
 
 // ------------------------------------------------------------ tile I/O --
@@ -465,7 +486,8 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     // only wave 0 uses it, so only wave 0 pays for it on the CU's scalar unit.
     uint64_t word = 0;
     if (wid == 0 && a.uid) word = request_word(a.seed, ld_global<int64_t>(a.uid + b), a.step);
-    const double u = uniform24(word);
+    if (threadIdx.x == 0) ss.word = word;   // for the other waves, after the next barrier
+    const double u = uniform24(word);       // valid in wave 0
     const int n_tiles = (V + IO::TILE - 1) / IO::TILE;
 
     int mode;
@@ -588,6 +610,10 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         if (threadIdx.x < kMaxTiles) {
             ss.tacc[threadIdx.x] = 0.0;
             ss.tcnt[threadIdx.x] = 0;
+        }
+        if (threadIdx.x < kList) {
+            ss.rankp[threadIdx.x] = 0u;
+            ss.ranki[threadIdx.x] = 0u;
         }
         // theta: lower edge of the histogram bin holding the j-th largest of
         // the per-thread maxima of the first tiles
@@ -1241,9 +1267,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             auto step = [&](uint32_t done_type) -> PassDesc {
                 if (first_p) {
                     // the softmax normaliser of a top-p row
-                    double z = 0.0;
-#pragma unroll
-                    for (int w = 0; w < kWaves; ++w) z += ss.wd[w];
+                    const double z = wave_sum_dpp(lane < kWaves ? ss.wd[lane] : 0.0);
                     target = static_cast<double>(prm.p) * z;
                 }
                 if (done_type == kPassHistW || done_type == kPassHist) {
@@ -1346,8 +1370,292 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 return mk(kPassDone);
             };
 
-            PassDesc pd = mk(kPassHistW);
+            // ------------------------------------------------ block-parallel routes --
+            // The common cases finish with block-wide steps whose serial parts are
+            // short: a single wave executes about one dependent instruction per
+            // 10-15 cycles here, so long wave-0 sequences are what the tail costs.
+            //   S (top-k <= 64, top-p optional): pick the bin of the k-th entry,
+            //     list every entry at or above that bin (<= 64), rank the list in
+            //     descending and in token order at once; cut, top-p and the draw
+            //     are then scans over the list in wave 0.
+            //   P (top-p without top-k): pick the bin where the descending weight
+            //     reaches p * Z; list that bin while adding the weight of the
+            //     bins above it per tile; rank the list, cut, add the kept part;
+            //     then the draw scans the per-tile weights block-wide.
+            // Anything else (a boundary bin of more than kList entries, top-k
+            // above kList with top-p) goes to the pass-driven descent below.
+            const int sh_tile = kTileShift;
+            auto block_pick = [&](bool by_mass, uint32_t r, double tgt) -> BlockPick {
+                const int d = wid * kWave + (kWave - 1 - lane);   // lane 0: the wave's top bin
+                const uint32_t cb = ss.hcnt[d];
+                const double mb = ss.hmass[d];
+                const uint32_t sc = wave_scan_u32_dpp(cb);
+                const double sm = wave_scan_f64_dpp(mb);
+                if (lane == kWave - 1) {
+                    ss.wtc[wid] = sc;
+                    ss.wtm[wid] = sm;
+                }
+                __syncthreads();
+                // every wave scans the 16 wave totals the same way (lane l holds
+                // wave 15 - l, from the top bins down), so all agree on the wave
+                // that holds the pick
+                const int wl = kWaves - 1 - lane;
+                const uint32_t tc = lane < kWaves ? ss.wtc[wl] : 0u;
+                const double tm = lane < kWaves ? ss.wtm[wl] : 0.0;
+                const uint32_t tci = wave_scan_u32_dpp(tc);
+                const double tmi = wave_scan_f64_dpp(tm);
+                const uint64_t wb = __ballot(lane < kWaves && tc != 0u && (by_mass ? tmi >= tgt : tci >= r));
+                int cross = wb ? kWaves - 1 - (__ffsll(static_cast<unsigned long long>(wb)) - 1) : -1;
+                if (cross < 0 && by_mass) {
+                    // rounding at the very end: the lowest non-empty wave if the
+                    // total reaches the target
+                    const uint64_t nzw = __ballot(lane < kWaves && tc != 0u);
+                    const double tot = readlane_f64(tmi, kWaves - 1);
+                    if (nzw && tot >= tgt) cross = kWaves - 1 - (63 - __clzll(static_cast<long long>(nzw)));
+                }
+                const uint32_t acw = readlane_u32(tci - tc, kWaves - 1 - wid);
+                const double amw = readlane_f64(tmi - tm, kWaves - 1 - wid);
+                if (wid == cross) {
+                    const bool hit = cb != 0u && (by_mass ? amw + sm >= tgt : acw + sc >= r);
+                    uint64_t bal = __ballot(hit);
+                    if (bal == 0ull) {      // rounding: the wave's lowest non-empty bin
+                        const uint64_t nz = __ballot(cb != 0u);
+                        bal = nz ? (1ull << (63 - __clzll(static_cast<long long>(nz)))) : 0ull;
+                    }
+                    if (lane == __ffsll(static_cast<unsigned long long>(bal)) - 1) {
+                        ss.pick.d = d;
+                        ss.pick.cnt = cb;
+                        ss.pick.above_c = acw + sc - cb;
+                        ss.pick.mass = mb;
+                        ss.pick.above_m = amw + (sm - mb);
+                    }
+                }
+                if (cross < 0 && threadIdx.x == 0) ss.pick.d = -1;
+                __syncthreads();
+                return ss.pick;
+            };
+            // list the entries with key in [glo, ghi]; entries with key > tabove
+            // add their weight to their tile
+            auto gather_pass = [&](uint32_t glo, uint32_t ghi, uint32_t tabove) {
+                const int rbase = wid * kRegion;
+                const uint32_t n = cnt < static_cast<uint32_t>(kRegion) ? cnt : static_cast<uint32_t>(kRegion);
+                for (uint32_t i = lane; i < n; i += kWave) {
+                    const int sl = rbase + static_cast<int>(i);
+                    const uint2 en = ss.cent[sl];
+                    if (en.x >= glo && en.x <= ghi) {
+                        const uint32_t p = atomicAdd(&ss.list_n, 1u);
+                        if (p < static_cast<uint32_t>(kList)) {
+                            ss.lkey[p] = en.x;
+                            ss.lidx[p] = en.y;
+                            ss.lw[p] = ss.cw[sl];
+                        }
+                    } else if (en.x > tabove) {
+                        atomicAdd(&ss.tacc[en.y >> sh_tile], static_cast<double>(ss.cw[sl]));
+                    }
+                }
+                __syncthreads();
+            };
+            // ranks of the listed entries: wave w compares every entry with
+            // entries 4w .. 4w+3
+            auto block_rank = [&]() {
+                const int n = ss.list_n < static_cast<uint32_t>(kList) ? static_cast<int>(ss.list_n) : kList;
+                if (lane < n && kWave / kWaves * wid < n) {
+                    const uint32_t k0 = ss.lkey[lane], i0 = ss.lidx[lane];
+                    uint32_t rp = 0, ri = 0;
+                    const int j1 = kList / kWaves * (wid + 1) < n ? kList / kWaves * (wid + 1) : n;
+                    for (int j = kList / kWaves * wid; j < j1; ++j) {
+                        const uint32_t k2 = ss.lkey[j], i2 = ss.lidx[j];
+                        rp += (k2 > k0 || (k2 == k0 && i2 < i0)) ? 1u : 0u;
+                        ri += i2 < i0 ? 1u : 0u;
+                    }
+                    if (rp) atomicAdd(&ss.rankp[lane], rp);
+                    if (ri) atomicAdd(&ss.ranki[lane], ri);
+                }
+                __syncthreads();
+            };
+            // wave 0: place the ranked list (descending order into skey/sidx/sw,
+            // token order into xrp/xw/xidx) and clear the ranks and the list
+            auto w0_place = [&](int n) {
+                if (lane < n) {
+                    const uint32_t rp = ss.rankp[lane], ri = ss.ranki[lane];
+                    const uint32_t k0 = ss.lkey[lane], i0 = ss.lidx[lane];
+                    const float w0 = ss.lw[lane];
+                    ss.skey[rp] = k0;
+                    ss.sidx[rp] = i0;
+                    ss.sw[rp] = w0;
+                    ss.xrp[ri] = rp;
+                    ss.xw[ri] = w0;
+                    ss.xidx[ri] = i0;
+                    ss.rankp[lane] = 0u;
+                    ss.ranki[lane] = 0u;
+                }
+                if (lane == 0) ss.list_n = 0u;
+                wave_lds_sync();
+            };
+            // block-wide draw from the per-tile kept weights (cleared here): the
+            // wave holding the first tile whose prefix exceeds u * W walks that
+            // tile's entries kept by ct in token order
+            auto block_tile_draw = [&](const Cut& ct) {
+                constexpr int TPW = kMaxTiles / kWaves;
+                const int tb = wid * TPW;
+                double v = 0.0;
+                if (lane < TPW) {
+                    v = ss.tacc[tb + lane];
+                    ss.tacc[tb + lane] = 0.0;
+                }
+                const double incl = wave_scan_f64_dpp(v);
+                if (lane == kWave - 1) ss.wtm[wid] = incl;
+                __syncthreads();
+                // every wave scans the 16 wave totals the same way (lane l holds
+                // wave l, tiles ascending)
+                const double tw = lane < kWaves ? ss.wtm[lane] : 0.0;
+                const double twi = wave_scan_f64_dpp(tw);
+                const double total_pre = readlane_f64(twi, kWaves - 1);
+                const double tgt = uniform24(ss.word) * total_pre;   // every wave
+                const uint64_t wb = __ballot(lane < kWaves && tw > 0.0 && twi > tgt);
+                const uint64_t nzw = __ballot(lane < kWaves && tw > 0.0);
+                const int cross = wb ? __ffsll(static_cast<unsigned long long>(wb)) - 1
+                                     : (nzw ? 63 - __clzll(static_cast<long long>(nzw)) : -1);
+                const double before = readlane_f64(twi - tw, wid);
+                if (wid == cross) {
+                    const double cum = before + incl;
+                    const uint64_t hb = __ballot(v > 0.0 && cum > tgt);
+                    const uint64_t nz = __ballot(v > 0.0);
+                    const int lx = hb ? __ffsll(static_cast<unsigned long long>(hb)) - 1
+                                      : 63 - __clzll(static_cast<long long>(nz));
+                    const double rem = hb ? tgt - readlane_f64(before + (incl - v), lx) : INFINITY;
+                    const int ts = tb + lx;
+                    const int sb = (ts & (kWaves - 1)) * kRegion + ss.tstart[ts];
+                    const int n = ss.tcnt[ts];
+                    double run2 = 0.0;
+                    uint32_t found = 0xffffffffu, last = 0xffffffffu;
+                    for (int j0 = 0; j0 < n; j0 += kWave) {
+                        const int j = j0 + lane;
+                        double val = 0.0;
+                        uint32_t idx = 0;
+                        if (j < n) {
+                            const uint2 en = ss.cent[sb + j];
+                            idx = en.y;
+                            val = ct.keep(en.y, en.x) ? static_cast<double>(ss.cw[sb + j]) : 0.0;
+                        }
+                        const double in2 = wave_scan_f64_dpp(val);
+                        const uint64_t hit = __ballot(val > 0.0 && run2 + in2 > rem);
+                        const uint64_t pb = __ballot(val > 0.0);
+                        if (pb) last = readlane_u32(idx, 63 - __clzll(static_cast<long long>(pb)));
+                        if (hit) {
+                            found = readlane_u32(idx, __ffsll(static_cast<unsigned long long>(hit)) - 1);
+                            break;
+                        }
+                        run2 += readlane_f64(in2, kWave - 1);
+                    }
+                    if (lane == 0) {
+                        ss.res_token = found != 0xffffffffu ? found : last;
+                        ss.res_w = total_pre;
+                    }
+                }
+                __syncthreads();
+            };
+
+            // keys, weights and the histogram over [theta, m]
             if (threadIdx.x == 0) ss.list_n = 0u;
+            run_pass(mk(kPassHistW));
+            __syncthreads();
+            int route = 0;           // 0 general, 1 S, 2 P, 3 finish from the row
+            BlockPick bp{};
+            // the softmax normaliser of a top-p row (same value wherever it is used)
+            auto row_z = [&]() -> double {
+                return wave_sum_dpp(lane < kWaves ? ss.wd[lane] : 0.0);
+            };
+            const bool small_k = mode == kTopK && prm.k <= kList;
+            if (small_k) {
+                bp = block_pick(false, static_cast<uint32_t>(prm.k), 0.0);
+                if (bp.d >= 0 && bp.above_c + bp.cnt <= static_cast<uint32_t>(kList)) route = 1;
+            } else if (mode == kTopP) {
+                bp = block_pick(true, 0u, static_cast<double>(prm.p) * row_z());
+                if (bp.d < 0) route = 3;
+                else if (bp.cnt <= static_cast<uint32_t>(kList)) route = 2;
+            }
+            const uint32_t key_lo0 = lo;
+            const uint32_t blo = key_lo0 + (bp.d >= 0 ? static_cast<uint32_t>(bp.d) << sh : 0u);
+            const uint32_t bhi = bin_hi(blo, static_cast<int>(sh), key_hi);
+            if (route == 1) {
+                gather_pass(blo, key_hi, 0xffffffffu);
+                block_rank();
+                if (wid == 0) {
+                    const int n = static_cast<int>(ss.list_n);
+                    w0_place(n);
+                    const bool in = lane < n;
+                    const double w = in ? static_cast<double>(ss.sw[lane]) : 0.0;
+                    const double incl = wave_scan_f64_dpp(w);
+                    const int k = prm.k;
+                    int e = k - 1;
+                    if (prm.top_p) {
+                        const double target_p = static_cast<double>(prm.p) * readlane_f64(incl, k - 1);
+                        const uint64_t bal = __ballot(lane < k && incl >= target_p);
+                        if (bal) e = __ffsll(static_cast<unsigned long long>(bal)) - 1;
+                    }
+                    const uint32_t ck = readlane_u32(in ? ss.skey[lane] : 0u, e);
+                    const uint32_t cl = readlane_u32(in ? ss.sidx[lane] : 0u, e);
+                    // the draw over the kept entries in token order
+                    const double xv = in && ss.xrp[lane] <= static_cast<uint32_t>(e) ? static_cast<double>(ss.xw[lane]) : 0.0;
+                    const double xin = wave_scan_f64_dpp(xv);
+                    const double tot = readlane_f64(xin, kWave - 1);
+                    const double tg = u * tot;
+                    const uint64_t hit = __ballot(xv > 0.0 && xin > tg);
+                    const uint64_t nzb = __ballot(xv > 0.0);
+                    const int tl = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1
+                                       : (nzb ? 63 - __clzll(static_cast<long long>(nzb)) : 0);
+                    const uint32_t tok = readlane_u32(in ? ss.xidx[lane] : 0u, tl);
+                    if (lane == 0) {
+                        ss.res_token = tok;
+                        ss.res_kept = static_cast<uint32_t>(e + 1);
+                        ss.res_w = tot;
+                        ss.cut_key = ck;
+                        ss.cut_last = cl;
+                    }
+                }
+                __syncthreads();
+            } else if (route == 2) {
+                gather_pass(blo, bhi, bhi);
+                block_rank();
+                if (wid == 0) {
+                    const int n = static_cast<int>(ss.list_n);
+                    w0_place(n);
+                    const bool in = lane < n;
+                    const double w = in ? static_cast<double>(ss.sw[lane]) : 0.0;
+                    const double incl = wave_scan_f64_dpp(w);
+                    const double target_p = static_cast<double>(prm.p) * row_z();
+                    const uint64_t bal = __ballot(in && bp.above_m + incl >= target_p);
+                    const int e = bal ? __ffsll(static_cast<unsigned long long>(bal)) - 1 : n - 1;
+                    if (in && lane <= e)
+                        atomicAdd(&ss.tacc[ss.sidx[lane] >> sh_tile], static_cast<double>(ss.sw[lane]));
+                    const uint32_t ck = readlane_u32(in ? ss.skey[lane] : 0u, e);
+                    const uint32_t cl = readlane_u32(in ? ss.sidx[lane] : 0u, e);
+                    if (lane == 0) {
+                        ss.res_token = amax;      // replaced by the draw
+                        ss.res_kept = bp.above_c + static_cast<uint32_t>(e) + 1u;
+                        ss.cut_key = ck;
+                        ss.cut_last = cl;
+                    }
+                }
+                __syncthreads();
+                block_tile_draw(Cut{ss.cut_key, ss.cut_last});
+            }
+            if (route == 1 || route == 2) {
+                fast = true;
+                cut = Cut{ss.cut_key, ss.cut_last};
+                token = ss.res_token;
+                n_kept = ss.res_kept;
+                W = ss.res_w;
+            } else if (route == 3) {
+                use_row = true;
+            } else {
+            // ------------------------------------------- pass-driven descent --
+            // keys and weights are in place: start from a fresh histogram
+            ss.hcnt[threadIdx.x] = 0u;
+            ss.hmass[threadIdx.x] = 0.0;
+            __syncthreads();
+            PassDesc pd = mk(kPassHist);
             for (;;) {
                 run_pass(pd);
                 __syncthreads();
@@ -1367,6 +1675,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 W = ss.res_w;
             } else {
                 use_row = true;
+            }
             }
         }
     }
