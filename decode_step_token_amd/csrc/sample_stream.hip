@@ -99,6 +99,8 @@ struct Smem {
     alignas(16) uint32_t hcnt[kBins];
     alignas(16) double hmass[kBins];
     PassDesc pass;
+    unsigned long long mbest;     // merge: packed (key, ~index) maximum
+    uint32_t mtotal, movf;        // merge: candidates stored, any region overflowed
     uint64_t word;                // the row's Philox word (written by wave 0)
     double res_w;
     uint32_t res_token, res_kept;
@@ -606,6 +608,11 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         if (t < n_tiles) IO::load(row, V, t, lane, raw);
         if (t + kWaves < n_tiles) IO::load(row, V, t + kWaves, lane, nxt);
     }
+    if (threadIdx.x == 0) {
+        ss.mbest = 0ull;
+        ss.mtotal = 0u;
+        ss.movf = 0u;
+    }
     if (want_cand) {
         if (threadIdx.x < kMaxTiles) {
             ss.tacc[threadIdx.x] = 0.0;
@@ -650,16 +657,36 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         }
         const uint32_t lo = 0xffffffffu - lo_neg;
         if (nv >= j) {
-            const int sh = range_shift(hi - lo);
-            if (key != 0u) atomicAdd(&ss.hcnt[(key - lo) >> sh], 1u);
-            __syncthreads();
-            if (wid == 0) {
-                uint32_t above = 0;
-                const int d = w0_desc_count(ss.hcnt, j, &above);
-                if (lane == 0) ss.bu[0] = lo + (static_cast<uint32_t>(d < 0 ? 0 : d) << sh);
+            // a bin holding many more maxima than needed (a wide key range, e.g.
+            // one negative lane maximum) is histogrammed again over its own range
+            uint32_t tlo = lo, thi = hi, jr = j, tkey = lo;
+            for (int round = 0; round < 3; ++round) {
+                const int sh = range_shift(thi - tlo);
+                if (key != 0u && key >= tlo && key <= thi) atomicAdd(&ss.hcnt[(key - tlo) >> sh], 1u);
+                __syncthreads();
+                if (wid == 0) {
+                    uint32_t above = 0;
+                    const int d = w0_desc_count(ss.hcnt, jr, &above);
+                    const uint32_t dd = static_cast<uint32_t>(d < 0 ? 0 : d);
+                    const uint32_t cd = ss.hcnt[dd];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ss.hcnt[4 * lane + i] = 0u;
+                    if (lane == 0) {
+                        const uint32_t blo_t = tlo + (dd << sh);
+                        ss.bu[0] = blo_t;
+                        ss.bu[1] = bin_hi(blo_t, sh, thi);
+                        ss.bu[2] = jr - above;
+                        ss.bu[3] = (round < 2 && sh > 0 && above + cd > 2u * jr) ? 1u : 0u;
+                    }
+                }
+                __syncthreads();
+                tkey = ss.bu[0];
+                if (ss.bu[3] == 0u) break;
+                tlo = ss.bu[0];
+                thi = ss.bu[1];
+                jr = ss.bu[2];
             }
-            __syncthreads();
-            theta = key_f32(ss.bu[0]);
+            theta = key_f32(tkey);
         } else {
             theta = -INFINITY;
         }
@@ -667,6 +694,8 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         // first use by the barrier after the stream)
         ss.hcnt[threadIdx.x] = 0u;
         ss.hmass[threadIdx.x] = 0.0;
+    } else {
+        __syncthreads();    // the merge slots above are set before any wave's merge
     }
     if (!use_row) {
         if (t < n_tiles) process(raw, t);
@@ -693,22 +722,16 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             pk = (static_cast<uint64_t>(f32_key(best_x)) << 32) | static_cast<uint64_t>(0xffffffffu - idx);
         }
         pk = wave_max_u64_dpp(pk);
-        __syncthreads();
         if (lane == 0) {
-            ss.wbest[wid] = pk;
-            ss.wcount[wid] = cnt;
+            atomicMax(reinterpret_cast<unsigned long long*>(&ss.mbest), static_cast<unsigned long long>(pk));
+            atomicAdd(&ss.mtotal, cnt < static_cast<uint32_t>(kRegion) ? cnt : static_cast<uint32_t>(kRegion));
+            if (cnt > static_cast<uint32_t>(kRegion)) atomicOr(&ss.movf, 1u);
         }
     }
     __syncthreads();
-    uint64_t best = 0;
-    uint32_t n_total = 0;
-    bool overflow = false;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        best = ss.wbest[w] > best ? ss.wbest[w] : best;
-        n_total += ss.wcount[w] < kRegion ? ss.wcount[w] : kRegion;
-        overflow |= ss.wcount[w] > kRegion;
-    }
+    const uint64_t best = ss.mbest;
+    const uint32_t n_total = ss.mtotal;
+    const bool overflow = ss.movf != 0u;
     const float m = key_f32(static_cast<uint32_t>(best >> 32));
     const uint32_t amax = 0xffffffffu - static_cast<uint32_t>(best);
     const double mc = static_cast<double>(m) * c;
