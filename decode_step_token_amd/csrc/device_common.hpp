@@ -164,6 +164,20 @@ __device__ __forceinline__ double uniform24(uint64_t word) {
     return static_cast<double>(word >> 40) * (1.0 / 16777216.0);
 }
 
+// ------------------------------------------------------------ barriers --
+// A workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load of the wave (its release fence covers all
+// address spaces), which drains a prefetch that is still in flight; this one
+// waits for the wave's LDS operations alone (s_waitcnt lgkmcnt(0): vmcnt and
+// expcnt fields at their maximum) and keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+}
+
 // ------------------------------------------------- DPP wave64 reductions --
 // Cross-lane data movement through DPP (no LDS round trip): quad swaps, row
 // half-mirror and mirror combine within a 16-lane row, then row_bcast15 /

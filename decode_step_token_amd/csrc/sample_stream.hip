@@ -647,7 +647,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             ss.wu[wid] = kmin_neg;
             ss.wcount[wid] = nval;
         }
-        __syncthreads();
+        lds_barrier();
         uint32_t hi = 0, lo_neg = 0, nv = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
@@ -663,7 +663,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             for (int round = 0; round < 3; ++round) {
                 const int sh = range_shift(thi - tlo);
                 if (key != 0u && key >= tlo && key <= thi) atomicAdd(&ss.hcnt[(key - tlo) >> sh], 1u);
-                __syncthreads();
+                lds_barrier();
                 if (wid == 0) {
                     uint32_t above = 0;
                     const int d = w0_desc_count(ss.hcnt, jr, &above);
@@ -679,7 +679,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                         ss.bu[3] = (round < 2 && sh > 0 && above + cd > 2u * jr) ? 1u : 0u;
                     }
                 }
-                __syncthreads();
+                lds_barrier();
                 tkey = ss.bu[0];
                 if (ss.bu[3] == 0u) break;
                 tlo = ss.bu[0];
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         ss.hcnt[threadIdx.x] = 0u;
         ss.hmass[threadIdx.x] = 0.0;
     } else {
-        __syncthreads();    // the merge slots above are set before any wave's merge
+        lds_barrier();      // the merge slots above are set before any wave's merge
     }
     if (!use_row) {
         if (t < n_tiles) process(raw, t);
