@@ -46,6 +46,7 @@ struct WriteArgs {
     const int32_t* tokens;
     int B;
     uint32_t* status;          // mapped pinned host word; set to 1 on a bad (row, col)
+    int32_t* host;             // device address of the pinned host copy, or null
 };
 
 hipError_t launch_argmax(const ArgmaxArgs& args, int dtype, hipStream_t stream);

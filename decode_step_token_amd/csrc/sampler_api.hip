@@ -212,22 +212,23 @@ int write_tokens(dst_sampler* s, void* stream, int32_t* token_pool, int64_t pool
         return fail(s, SAMPLER_EINVAL, "write_tokens: null pointer");
     if (pool_rows < 1 || pool_cols < 1) return fail(s, SAMPLER_EINVAL, "write_tokens: empty pool");
     DeviceGuard g(s->device);
+    int32_t* host_dev = nullptr;     // the pinned buffer as the device addresses it
     if (host_pinned_out && B > 0) {
         hipPointerAttribute_t attr;
         std::memset(&attr, 0, sizeof(attr));
         const hipError_t pe = hipPointerGetAttributes(&attr, host_pinned_out);
         if (pe != hipSuccess) (void)hipGetLastError();
-        if (pe != hipSuccess || attr.type != hipMemoryTypeHost)
+        if (pe != hipSuccess || attr.type != hipMemoryTypeHost || !attr.devicePointer)
             return fail(s, SAMPLER_ENOTPINNED, "write_tokens: host_pinned_out is not pinned host memory");
+        host_dev = static_cast<int32_t*>(attr.devicePointer);
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     if (B > 0) {
-        dst::WriteArgs a{token_pool, pool_rows, pool_cols, rows, cols, tokens, B, s->status_dev};
+        // one kernel: pool scatter plus the tokens stored straight into the
+        // pinned buffer (system-scope stores), no separate copy
+        dst::WriteArgs a{token_pool, pool_rows, pool_cols, rows, cols, tokens, B, s->status_dev, host_dev};
         e = dst::launch_write_tokens(a, st);
-        if (e == hipSuccess && host_pinned_out)
-            e = hipMemcpyAsync(host_pinned_out, tokens, sizeof(int32_t) * static_cast<size_t>(B),
-                               hipMemcpyDeviceToHost, st);
     }
     const uint64_t ticket = s->issued + 1;
     if (e == hipSuccess) e = hipEventRecord(s->ring[ticket % kRing], st);

@@ -9,6 +9,9 @@
 //
 // One thread per request; an out-of-range (row, col) skips the write and
 // raises the handle's status word (mapped pinned host memory, plain store).
+// The host copy of forward_batch is the same kernel: each thread also stores
+// its token into the caller's pinned buffer through its device mapping, with
+// system scope, so the completion event covers it.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -23,12 +26,14 @@ __global__ __launch_bounds__(kWriteBlock) void write_tokens_kernel(WriteArgs a) 
     if (b >= a.B) return;
     const int64_t r = a.rows[b];
     int64_t c = a.cols[b];
+    const int32_t tok = a.tokens[b];
     if (c == -1) c = a.pool_cols - 1;
     if (r >= 0 && r < a.pool_rows && c >= 0 && c < a.pool_cols) {
-        a.pool[r * a.pool_cols + c] = a.tokens[b];
+        a.pool[r * a.pool_cols + c] = tok;
     } else {
         *reinterpret_cast<volatile uint32_t*>(a.status) = 1u;
     }
+    if (a.host) __hip_atomic_store(a.host + b, tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 }  // namespace
