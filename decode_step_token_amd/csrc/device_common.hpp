@@ -34,6 +34,14 @@ __device__ __forceinline__ uint4 ld_global_u4(const void* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 16-byte streaming load: the line is not kept in the caches for reuse, so a
+// row read once does not push other lines (instructions, tables) out of L2.
+__device__ __forceinline__ uint4 ld_global_u4_stream(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(
+        reinterpret_cast<const __attribute__((address_space(1))) u32x4_t*>(reinterpret_cast<uintptr_t>(p)));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---------------------------------------------------------------- values --
 
 // Order-preserving 32-bit key of a float: larger float -> larger key; -0.0

@@ -69,6 +69,8 @@ enum PassType : uint32_t {
     kPassTileMass,    // per-tile weight of the entries kept by the restriction
     kPassDone,
     kPassFallback,    // the kept prefix reaches below theta: finish from the row
+    kPassHistC,       // order keys and the count histogram only
+    kPassWeights,     // weights of all entries
 };
 
 struct PassDesc {
@@ -146,7 +148,7 @@ struct TileIO {
         for (int u = 0; u < U; ++u) {
             const int64_t off = base + u * kWave * VEC + lane * VEC;
             if (off + VEC <= V) {
-                raw[u] = ld_global_u4(static_cast<const char*>(row) + off * (DT == kDtypeF32 ? 4 : 2));
+                raw[u] = ld_global_u4_stream(static_cast<const char*>(row) + off * (DT == kDtypeF32 ? 4 : 2));
             } else {
                 uint32_t w[4];
                 if (DT == kDtypeF32) {
@@ -514,6 +516,13 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
 
     float lref = -INFINITY;           // top-p rows: this lane's running reference
     double lsum = 0.0;                // ... and its exponent sum relative to it
+    // The candidate histogram is built by each wave right after its own
+    // stream, before the row maximum is known: bins over [theta, m0] (m0 =
+    // the largest value of the first tiles; keys above it land in the top
+    // bin), top-p weights relative to m0.
+    bool pre = false;
+    uint32_t pre_lo = 0, pre_sh = 0;
+    float m0 = -INFINITY;
 
     auto process = [&](const uint4* raw, int t) {
         float tmax = IO::get(raw, 0);
@@ -612,6 +621,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         ss.mbest = 0ull;
         ss.mtotal = 0u;
         ss.movf = 0u;
+        ss.list_n = 0u;
     }
     if (want_cand) {
         if (threadIdx.x < kMaxTiles) {
@@ -641,7 +651,9 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         const uint32_t kmax = wave_max_u32_dpp(key);
         const uint32_t kmin_neg = wave_max_u32_dpp(key ? 0xffffffffu - key : 0u);
         const uint32_t nval = static_cast<uint32_t>(__popcll(__ballot(key != 0u)));
-        if (threadIdx.x < 256) ss.hcnt[threadIdx.x] = 0;
+        // all bins start empty; the rounds below leave them empty again
+        ss.hcnt[threadIdx.x] = 0u;
+        ss.hmass[threadIdx.x] = 0.0;
         if (lane == 0) {
             ss.wbest[wid] = kmax;
             ss.wu[wid] = kmin_neg;
@@ -687,13 +699,13 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 jr = ss.bu[2];
             }
             theta = key_f32(tkey);
+            pre = hi >= tkey;
+            pre_lo = tkey;
+            pre_sh = static_cast<uint32_t>(range_shift_bins(hi - tkey));
+            m0 = key_f32(hi);
         } else {
             theta = -INFINITY;
         }
-        // the candidate tail's histogram starts empty (ordered before its
-        // first use by the barrier after the stream)
-        ss.hcnt[threadIdx.x] = 0u;
-        ss.hmass[threadIdx.x] = 0.0;
     } else {
         lds_barrier();      // the merge slots above are set before any wave's merge
     }
@@ -712,6 +724,36 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             if (x > best_x) { best_x = x; best_t = i; }
         }
         best_q = -1;
+    }
+
+    // ------------------------------- this wave's share of the candidate tail --
+    // top-p: the lane sums relative to m0; every candidate row: order keys and
+    // the count histogram of this wave's region, top-p rows also weights
+    // relative to m0 and the mass histogram
+    const double m0c = static_cast<double>(m0) * c;
+    if (want_lanez && pre) {
+        const double part = lsum > 0.0
+            ? lsum * exp2_neg((static_cast<double>(lref) - static_cast<double>(m0)) * c) : 0.0;
+        const double ws = wave_sum_dpp(part);
+        if (lane == 0) ss.wd[wid] = ws;
+    }
+    if (pre) {
+        const int rbase = wid * kRegion;
+        const uint32_t n = cnt < static_cast<uint32_t>(kRegion) ? cnt : static_cast<uint32_t>(kRegion);
+        for (uint32_t i = lane; i < n; i += kWave) {
+            const int sl = rbase + static_cast<int>(i);
+            const float x = __uint_as_float(ss.cent[sl].x);
+            const uint32_t key = f32_key(x);
+            ss.cent[sl].x = key;
+            const uint32_t d0 = (key - pre_lo) >> pre_sh;
+            const uint32_t d = d0 < static_cast<uint32_t>(kBins - 1) ? d0 : static_cast<uint32_t>(kBins - 1);
+            atomicAdd(&ss.hcnt[d], 1u);
+            if (want_lanez) {
+                const float w = static_cast<float>(fast_weight(x, m0c, c));
+                ss.cw[sl] = w;
+                atomicAdd(&ss.hmass[d], static_cast<double>(w));
+            }
+        }
     }
 
     // --------------------------------------------- row maximum and argmax --
@@ -734,7 +776,11 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     const bool overflow = ss.movf != 0u;
     const float m = key_f32(static_cast<uint32_t>(best >> 32));
     const uint32_t amax = 0xffffffffu - static_cast<uint32_t>(best);
-    const double mc = static_cast<double>(m) * c;
+    // top-p rows keep m0 as the weight reference while every weight relative
+    // to it stays far below the float range; otherwise the row maximum
+    const bool pre_ok = pre && (mode != kTopP ||
+                                (static_cast<double>(m) - static_cast<double>(m0)) * c <= 64.0);
+    const double mc = mode == kTopP && pre_ok ? m0c : static_cast<double>(m) * c;
     int32_t* topk_out = a.topk_idx_out ? a.topk_idx_out + static_cast<int64_t>(b) * kDebugTopK : nullptr;
 
     if (mode == kArgmax) {
@@ -1097,9 +1143,9 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             return;
         }
     }
-    // top-p rows: the per-lane sums rescaled to the row maximum; wave 0 adds
-    // the wave partials once the next barrier has passed
-    if (want_lanez) {
+    // top-p rows without the m0 reference: the per-lane sums rescaled to the
+    // row maximum (read after the next barrier)
+    if (want_lanez && !pre_ok) {
         const double part = lsum > 0.0
             ? lsum * exp2_neg((static_cast<double>(lref) - static_cast<double>(m)) * c) : 0.0;
         const double ws = wave_sum_dpp(part);
@@ -1155,16 +1201,22 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 const Cut rcut{pd.rkey, pd.rlast};
                 for (uint32_t i = lane; i < n; i += kWave) {
                     const int sl = rbase + static_cast<int>(i);
-                    if (pd.type == kPassHistW) {
+                    if (pd.type == kPassHistW || pd.type == kPassHistC) {
                         // the stream stored raw value bits: turn them into order keys
                         const float x = __uint_as_float(ss.cent[sl].x);
                         const uint32_t key = f32_key(x);
                         ss.cent[sl].x = key;
-                        const float w = static_cast<float>(fast_weight(x, mc, c));
-                        ss.cw[sl] = w;
                         const uint32_t d = (key - pd.lo) >> pd.sh;
                         atomicAdd(&ss.hcnt[d], 1u);
-                        atomicAdd(&ss.hmass[d], static_cast<double>(w));
+                        if (pd.type == kPassHistW) {
+                            const float w = static_cast<float>(fast_weight(x, mc, c));
+                            ss.cw[sl] = w;
+                            atomicAdd(&ss.hmass[d], static_cast<double>(w));
+                        }
+                        continue;
+                    }
+                    if (pd.type == kPassWeights) {
+                        ss.cw[sl] = static_cast<float>(fast_weight(key_f32(ss.cent[sl].x), mc, c));
                         continue;
                     }
                     const uint32_t key = ss.cent[sl].x;
@@ -1411,12 +1463,12 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             auto block_pick = [&](bool by_mass, uint32_t r, double tgt) -> BlockPick {
                 const int d = wid * kWave + (kWave - 1 - lane);   // lane 0: the wave's top bin
                 const uint32_t cb = ss.hcnt[d];
-                const double mb = ss.hmass[d];
+                const double mb = by_mass ? ss.hmass[d] : 0.0;
                 const uint32_t sc = wave_scan_u32_dpp(cb);
-                const double sm = wave_scan_f64_dpp(mb);
+                const double sm = by_mass ? wave_scan_f64_dpp(mb) : 0.0;
                 if (lane == kWave - 1) {
                     ss.wtc[wid] = sc;
-                    ss.wtm[wid] = sm;
+                    if (by_mass) ss.wtm[wid] = sm;
                 }
                 __syncthreads();
                 // every wave scans the 16 wave totals the same way (lane l holds
@@ -1424,9 +1476,9 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 // that holds the pick
                 const int wl = kWaves - 1 - lane;
                 const uint32_t tc = lane < kWaves ? ss.wtc[wl] : 0u;
-                const double tm = lane < kWaves ? ss.wtm[wl] : 0.0;
+                const double tm = by_mass && lane < kWaves ? ss.wtm[wl] : 0.0;
                 const uint32_t tci = wave_scan_u32_dpp(tc);
-                const double tmi = wave_scan_f64_dpp(tm);
+                const double tmi = by_mass ? wave_scan_f64_dpp(tm) : 0.0;
                 const uint64_t wb = __ballot(lane < kWaves && tc != 0u && (by_mass ? tmi >= tgt : tci >= r));
                 int cross = wb ? kWaves - 1 - (__ffsll(static_cast<unsigned long long>(wb)) - 1) : -1;
                 if (cross < 0 && by_mass) {
@@ -1437,7 +1489,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                     if (nzw && tot >= tgt) cross = kWaves - 1 - (63 - __clzll(static_cast<long long>(nzw)));
                 }
                 const uint32_t acw = readlane_u32(tci - tc, kWaves - 1 - wid);
-                const double amw = readlane_f64(tmi - tm, kWaves - 1 - wid);
+                const double amw = by_mass ? readlane_f64(tmi - tm, kWaves - 1 - wid) : 0.0;
                 if (wid == cross) {
                     const bool hit = cb != 0u && (by_mass ? amw + sm >= tgt : acw + sc >= r);
                     uint64_t bal = __ballot(hit);
@@ -1470,7 +1522,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                         if (p < static_cast<uint32_t>(kList)) {
                             ss.lkey[p] = en.x;
                             ss.lidx[p] = en.y;
-                            ss.lw[p] = ss.cw[sl];
+                            ss.lw[p] = static_cast<float>(fast_weight(key_f32(en.x), mc, c));
                         }
                     } else if (en.x > tabove) {
                         atomicAdd(&ss.tacc[en.y >> sh_tile], static_cast<double>(ss.cw[sl]));
@@ -1579,17 +1631,34 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 __syncthreads();
             };
 
-            // keys, weights and the histogram over [theta, m]
-            if (threadIdx.x == 0) ss.list_n = 0u;
-            run_pass(mk(kPassHistW));
-            __syncthreads();
+            // The histogram the routes pick from: the one each wave built after
+            // its stream (bins of width 2^pre_sh from theta, the top bin reaching
+            // up to m), else one built now over [theta, m].  Top-k rows only
+            // count; their weights are computed where they are needed.
+            const bool small_k = mode == kTopK && prm.k <= kList;
+            uint32_t hsh = pre_sh;
+            bool top_ext = true;
+            if (!pre_ok) {
+                ss.hcnt[threadIdx.x] = 0u;
+                ss.hmass[threadIdx.x] = 0.0;
+                __syncthreads();
+                if (pre) {
+                    // keys are in place: weights relative to m, then the histogram
+                    if (mode == kTopP) run_pass(mk(kPassWeights));
+                    run_pass(mk(kPassHist));
+                } else {
+                    run_pass(mk(mode == kTopP ? kPassHistW : kPassHistC));
+                }
+                __syncthreads();
+                hsh = sh;
+                top_ext = false;
+            }
             int route = 0;           // 0 general, 1 S, 2 P, 3 finish from the row
             BlockPick bp{};
             // the softmax normaliser of a top-p row (same value wherever it is used)
             auto row_z = [&]() -> double {
                 return wave_sum_dpp(lane < kWaves ? ss.wd[lane] : 0.0);
             };
-            const bool small_k = mode == kTopK && prm.k <= kList;
             if (small_k) {
                 bp = block_pick(false, static_cast<uint32_t>(prm.k), 0.0);
                 if (bp.d >= 0 && bp.above_c + bp.cnt <= static_cast<uint32_t>(kList)) route = 1;
@@ -1599,8 +1668,8 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 else if (bp.cnt <= static_cast<uint32_t>(kList)) route = 2;
             }
             const uint32_t key_lo0 = lo;
-            const uint32_t blo = key_lo0 + (bp.d >= 0 ? static_cast<uint32_t>(bp.d) << sh : 0u);
-            const uint32_t bhi = bin_hi(blo, static_cast<int>(sh), key_hi);
+            const uint32_t blo = key_lo0 + (bp.d >= 0 ? static_cast<uint32_t>(bp.d) << hsh : 0u);
+            const uint32_t bhi = top_ext && bp.d == kBins - 1 ? key_hi : bin_hi(blo, static_cast<int>(hsh), key_hi);
             if (route == 1) {
                 gather_pass(blo, key_hi, 0xffffffffu);
                 block_rank();
@@ -1674,7 +1743,9 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 use_row = true;
             } else {
             // ------------------------------------------- pass-driven descent --
-            // keys and weights are in place: start from a fresh histogram
+            // keys are in place (and weights, unless only counted so far):
+            // start from a fresh histogram
+            if (mode == kTopK) run_pass(mk(kPassWeights));
             ss.hcnt[threadIdx.x] = 0u;
             ss.hmass[threadIdx.x] = 0.0;
             __syncthreads();
