@@ -529,12 +529,15 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
 #pragma unroll
         for (int q = 1; q < Q; ++q) tmax = fmaxf(tmax, IO::get(raw, q));
         if (tmax > best_x) {
-            int qq = Q - 1;
+            // the position inside the tile only matters to argmax rows
+            if (mode == kArgmax) {
+                int qq = Q - 1;
 #pragma unroll
-            for (int q = Q - 1; q >= 0; --q) qq = IO::get(raw, q) == tmax ? q : qq;
+                for (int q = Q - 1; q >= 0; --q) qq = IO::get(raw, q) == tmax ? q : qq;
+                best_q = qq;
+            }
             best_x = tmax;
             best_t = t;
-            best_q = qq;
         }
         if (want_tiles) {
             // tile-local reference: (x - tref) is exact for the logits that
@@ -551,9 +554,11 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             }
         }
         if (want_lanez) {
-            // the same argument per lane, against the lane's running maximum
-            // (online rescaling when it grows), accumulated in fp64
-            if (tmax > lref) {
+            // the same argument per lane, against a reference that starts at
+            // m0 (the first tiles' maximum) and is raised (the sum rescaled)
+            // only when a value exceeds it by more than 2^30 in weight, so the
+            // fp32 tile sums stay finite; accumulated in fp64
+            if ((tmax - lref) * c32 > 30.0f) {
                 if (lsum > 0.0) lsum *= exp2_neg((static_cast<double>(lref) - static_cast<double>(tmax)) * c);
                 lref = tmax;
             }
@@ -703,6 +708,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             pre_lo = tkey;
             pre_sh = static_cast<uint32_t>(range_shift_bins(hi - tkey));
             m0 = key_f32(hi);
+            lref = m0;
         } else {
             theta = -INFINITY;
         }

@@ -88,6 +88,25 @@ def test_extreme_temperatures_and_parameters():
     _check(w)
 
 
+def test_late_maximum_weight_reference():
+    """Top-p rows whose maximum lies beyond the first tiles: with a small gap
+    the weights stay relative to the first tiles' maximum, with a large gap
+    (relative to the temperature) they switch to the row maximum; both must
+    match the oracle, and so must top-k rows with the same rows."""
+    rng = np.random.default_rng(17)
+    B, V = 24, 40000
+    w = wl.tiny(rng, B, V, "f32")
+    for b in range(B):
+        top = float(w.logits[b].max())
+        j = int(rng.integers(20000, V))
+        w.logits[b, j] = np.float32(top + (8.0 if b % 3 == 0 else 1.5 if b % 3 == 1 else 0.0))
+    w.temperature[:] = np.array([0.05, 0.5, 1.0] * 8, dtype=np.float32)
+    w.top_k[:] = -1
+    w.top_k[18:] = np.array([20, 50, 64, 65, 500, 3], dtype=np.int32)
+    w.top_p[:] = np.array([0.9, 0.5, 0.99, 0.8, 0.95, 0.3] * 4, dtype=np.float32)
+    _check(w)
+
+
 def test_greedy_batch_without_temperature_bf16():
     rng = np.random.default_rng(13)
     w = wl.tiny(rng, 100, 7000, "bf16")
