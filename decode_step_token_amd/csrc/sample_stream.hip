@@ -91,7 +91,8 @@ struct BlockPick {
 };
 
 struct Smem {
-    uint2 cent[kCap];             // candidates: (value bits, later the order key; token index)
+    uint2 cent[kCap + kBlock];    // candidates: (value bits, later the order key; token index);
+                                  // the last kBlock entries: one discard slot per thread
     float cw[kCap];
     float tref[kMaxTiles];
     double tsum[kMaxTiles];
@@ -516,6 +517,10 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
 
     float lref = -INFINITY;           // top-p rows: this lane's running reference
     double lsum = 0.0;                // ... and its exponent sum relative to it
+    // Each exponent is one fma, x * c32 - lrc with lrc = lref * c32 rounded;
+    // that is (x - lref) * c32 + lrd, lrd = lref * c32 - lrc exactly, so the
+    // sum carries a factor 2^lrd that is taken out in fp64.
+    float lrc = -INFINITY, lrd = 0.0f;
     // The candidate histogram is built by each wave right after its own
     // stream, before the row maximum is known: bins over [theta, m0] (m0 =
     // the largest value of the first tiles; keys above it land in the top
@@ -559,12 +564,18 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             // only when a value exceeds it by more than 2^30 in weight, so the
             // fp32 tile sums stay finite; accumulated in fp64
             if ((tmax - lref) * c32 > 30.0f) {
-                if (lsum > 0.0) lsum *= exp2_neg((static_cast<double>(lref) - static_cast<double>(tmax)) * c);
+                const float nrc = tmax * c32;
+                const float nrd = fmaf(tmax, c32, -nrc);
+                if (lsum > 0.0)
+                    lsum *= exp2_neg((static_cast<double>(lref) - static_cast<double>(tmax)) * c
+                                     - static_cast<double>(lrd) + static_cast<double>(nrd));
                 lref = tmax;
+                lrc = nrc;
+                lrd = nrd;
             }
             float s = 0.0f;
 #pragma unroll
-            for (int q = 0; q < Q; ++q) s += __builtin_amdgcn_exp2f((IO::get(raw, q) - lref) * c32);
+            for (int q = 0; q < Q; ++q) s += __builtin_amdgcn_exp2f(fmaf(IO::get(raw, q), c32, -lrc));
             lsum += static_cast<double>(s);
         }
         if (want_cand && __ballot(tmax >= theta) != 0) {
@@ -593,19 +604,25 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 total += ((ex_last >> (FB * uu)) & FM) + ((pk_last >> (FB * uu)) & FM);
             if (cnt + total <= static_cast<uint32_t>(kRegion)) {
                 const uint32_t lanebase = IO::index(t, lane, 0);
+                const uint32_t discard = (static_cast<uint32_t>(kCap) + threadIdx.x) * static_cast<uint32_t>(sizeof(uint2));
                 uint32_t base = static_cast<uint32_t>(wid * kRegion) + cnt;
 #pragma unroll
                 for (int uu = 0; uu < IO::U; ++uu) {
-                    uint32_t pos = base + ((ex >> (FB * uu)) & FM);
+                    // a load without candidates in any lane is skipped; otherwise
+                    // every lane stores each element, non-candidates to its own
+                    // discard slot, so the stores need no branches
+                    const uint32_t cu_all = ((ex_last >> (FB * uu)) & FM) + ((pk_last >> (FB * uu)) & FM);
+                    if (cu_all == 0u) continue;
+                    uint32_t pos = (base + ((ex >> (FB * uu)) & FM)) * static_cast<uint32_t>(sizeof(uint2));
 #pragma unroll
                     for (int e = 0; e < IO::VEC; ++e) {
                         const float x = IO::get(raw, uu * IO::VEC + e);
-                        if (x >= theta) {
-                            ss.cent[pos] = make_uint2(__float_as_uint(x), lanebase + uu * kWave * IO::VEC + e);
-                            ++pos;
-                        }
+                        const bool is = x >= theta;
+                        *reinterpret_cast<uint2*>(reinterpret_cast<char*>(ss.cent) + (is ? pos : discard)) =
+                            make_uint2(__float_as_uint(x), lanebase + uu * kWave * IO::VEC + e);
+                        pos += is ? static_cast<uint32_t>(sizeof(uint2)) : 0u;
                     }
-                    base += ((ex_last >> (FB * uu)) & FM) + ((pk_last >> (FB * uu)) & FM);
+                    base += cu_all;
                 }
                 if (lane == 0) {
                     ss.tstart[t] = static_cast<uint16_t>(cnt);
@@ -616,11 +633,15 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         }
     };
 
+    // One tile ahead.  Candidate rows ask for their second tile only once the
+    // first has arrived: the theta selection below waits for the first tiles
+    // of all waves, which then come in sooner, and the second tiles stream
+    // in while it runs.
     uint4 raw[IO::U], nxt[IO::U];
     int t = wid;
     if (!use_row) {
         if (t < n_tiles) IO::load(row, V, t, lane, raw);
-        if (t + kWaves < n_tiles) IO::load(row, V, t + kWaves, lane, nxt);
+        if (!want_cand && t + kWaves < n_tiles) IO::load(row, V, t + kWaves, lane, nxt);
     }
     if (threadIdx.x == 0) {
         ss.mbest = 0ull;
@@ -644,6 +665,9 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
 #pragma unroll
             for (int q = 0; q < Q; ++q) lmax = fmaxf(lmax, IO::get(raw, q));
         }
+        // (the empty asm keeps the load below after the wait for the first tile)
+        asm volatile("" :: "v"(lmax) : "memory");
+        if (t + kWaves < n_tiles) IO::load(row, V, t + kWaves, lane, nxt);
         const uint32_t key = lmax > -INFINITY ? f32_key(lmax) : 0u;
         const int first_elems = V < kWaves * IO::TILE ? V : kWaves * IO::TILE;
         uint32_t j;
@@ -709,6 +733,8 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             pre_sh = static_cast<uint32_t>(range_shift_bins(hi - tkey));
             m0 = key_f32(hi);
             lref = m0;
+            lrc = m0 * c32;
+            lrd = fmaf(m0, c32, -lrc);
         } else {
             theta = -INFINITY;
         }
@@ -739,7 +765,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     const double m0c = static_cast<double>(m0) * c;
     if (want_lanez && pre) {
         const double part = lsum > 0.0
-            ? lsum * exp2_neg((static_cast<double>(lref) - static_cast<double>(m0)) * c) : 0.0;
+            ? lsum * exp2_neg((static_cast<double>(lref) - static_cast<double>(m0)) * c - static_cast<double>(lrd)) : 0.0;
         const double ws = wave_sum_dpp(part);
         if (lane == 0) ss.wd[wid] = ws;
     }
@@ -1153,7 +1179,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     // row maximum (read after the next barrier)
     if (want_lanez && !pre_ok) {
         const double part = lsum > 0.0
-            ? lsum * exp2_neg((static_cast<double>(lref) - static_cast<double>(m)) * c) : 0.0;
+            ? lsum * exp2_neg((static_cast<double>(lref) - static_cast<double>(m)) * c - static_cast<double>(lrd)) : 0.0;
         const double ws = wave_sum_dpp(part);
         if (lane == 0) ss.wd[wid] = ws;
     }
