@@ -1484,7 +1484,9 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             //   S (top-k <= 64, top-p optional): pick the bin of the k-th entry,
             //     list every entry at or above that bin (<= 64), rank the list in
             //     descending and in token order at once; cut, top-p and the draw
-            //     are then scans over the list in wave 0.
+            //     are then scans over the list in wave 0.  A top-p row whose
+            //     whole nucleus bin and the bins above it hold <= 64 entries
+            //     takes this route too.
             //   P (top-p without top-k): pick the bin where the descending weight
             //     reaches p * Z; list that bin while adding the weight of the
             //     bins above it per tile; rank the list, cut, add the kept part;
@@ -1697,6 +1699,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             } else if (mode == kTopP) {
                 bp = block_pick(true, 0u, static_cast<double>(prm.p) * row_z());
                 if (bp.d < 0) route = 3;
+                else if (bp.above_c + bp.cnt <= static_cast<uint32_t>(kList)) route = 1;   // the whole nucleus listed
                 else if (bp.cnt <= static_cast<uint32_t>(kList)) route = 2;
             }
             const uint32_t key_lo0 = lo;
@@ -1711,10 +1714,14 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                     const bool in = lane < n;
                     const double w = in ? static_cast<double>(ss.sw[lane]) : 0.0;
                     const double incl = wave_scan_f64_dpp(w);
-                    const int k = prm.k;
+                    // top-k: the first k, then top-p inside them; top-p alone: the
+                    // list holds every entry at or above the bin where the
+                    // descending weight reaches p * Z
+                    const int k = mode == kTopK ? prm.k : n;
                     int e = k - 1;
                     if (prm.top_p) {
-                        const double target_p = static_cast<double>(prm.p) * readlane_f64(incl, k - 1);
+                        const double target_p = static_cast<double>(prm.p) *
+                            (mode == kTopK ? readlane_f64(incl, k - 1) : row_z());
                         const uint64_t bal = __ballot(lane < k && incl >= target_p);
                         if (bal) e = __ffsll(static_cast<unsigned long long>(bal)) - 1;
                     }
