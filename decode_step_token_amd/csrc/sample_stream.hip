@@ -520,7 +520,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     // Each exponent is one fma, x * c32 - lrc with lrc = lref * c32 rounded;
     // that is (x - lref) * c32 + lrd, lrd = lref * c32 - lrc exactly, so the
     // sum carries a factor 2^lrd that is taken out in fp64.
-    float lrc = -INFINITY, lrd = 0.0f;
+    float lrc = INFINITY, lrd = 0.0f;
     // The candidate histogram is built by each wave right after its own
     // stream, before the row maximum is known: bins over [theta, m0] (m0 =
     // the largest value of the first tiles; keys above it land in the top
@@ -563,7 +563,9 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             // m0 (the first tiles' maximum) and is raised (the sum rescaled)
             // only when a value exceeds it by more than 2^30 in weight, so the
             // fp32 tile sums stay finite; accumulated in fp64
-            if ((tmax - lref) * c32 > 30.0f) {
+            // (a lane whose values so far are all padding (-inf) has no
+            // reference yet; its lrc of +inf makes them add exactly 0)
+            if (tmax > lref && (tmax - lref) * c32 > 30.0f) {
                 const float nrc = tmax * c32;
                 const float nrd = fmaf(tmax, c32, -nrc);
                 if (lsum > 0.0)
@@ -848,8 +850,16 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 f(f32_key(Elem<DT>::at(row, i)), i, -1);
         }
     };
+    // Weights of entries read from the row: one fma and one fp32 exp2,
+    // 2^(x*c32 - Pf) with Pf = mref*c32 rounded, times G = 2^-(mref*c32 - Pf)
+    // (the rounding, exact through fma) in fp64: the weight relative to the
+    // reference mref (mc = mref*c) with c rounded to fp32; fp64 sums.
+    const float mref = mode == kTopP && pre_ok ? m0 : m;
+    const float Pf = mref * c32;
+    const double G = exp2_neg(-static_cast<double>(fmaf(mref, c32, -Pf)));
     auto weight_of = [&](uint32_t k, int slot) -> double {
-        return slot >= 0 ? static_cast<double>(ss.cw[slot]) : fast_weight(key_f32(k), mc, c);
+        return slot >= 0 ? static_cast<double>(ss.cw[slot])
+                         : static_cast<double>(__builtin_amdgcn_exp2f(fmaf(key_f32(k), c32, -Pf))) * G;
     };
 
     // sum of weights (and count) over the entries inside `ct`
@@ -1009,22 +1019,28 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     };
 
     // The top-p cut inside `ct`: the descending-order prefix up to the first
-    // entry whose inclusive prefix mass reaches `target`.  false if the
-    // entries' mass never reaches it.
-    auto mass_cut = [&](const Cut& ct, double target, Cut* out) -> bool {
+    // entry whose inclusive prefix mass reaches `target`; also the kept
+    // weight and count.  false if the entries' mass never reaches it.
+    auto mass_cut = [&](const Cut& ct, double target, Cut* out, double* w_out, uint32_t* n_out) -> bool {
         auto pred = [&](uint32_t k, uint32_t i) { return ct.keep(i, k); };
         uint32_t lo, hi;
         key_range(ct, &lo, &hi);
         double above = 0.0;
+        uint32_t above_n = 0;
         for (;;) {
             const int sh = range_shift(hi - lo);
             histogram(pred, false, lo, hi, sh, true);
             if (wid == 0) {
                 double ab = 0.0;
                 const int d = w0_desc_mass(ss.hcnt, ss.hmass, above, target, &ab);
+                uint32_t ac = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ac += 4 * lane + i > d ? ss.hcnt[4 * lane + i] : 0u;
+                ac = readlane_u32(wave_scan_u32_dpp(ac), kWave - 1);
                 if (lane == 0) {
                     ss.bu[2] = static_cast<uint32_t>(d);
                     ss.bu[4] = d >= 0 ? ss.hcnt[d] : 0u;
+                    ss.bu[7] = ac;
                     ss.bd[1] = ab;
                 }
             }
@@ -1034,6 +1050,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             const double ab = ss.bd[1];
             if (d < 0) return false;
             above = ab;
+            above_n += ss.bu[7];
             const uint32_t nlo = lo + (static_cast<uint32_t>(d) << sh);
             const uint32_t nhi = bin_hi(nlo, sh, hi);
             if (cd <= static_cast<uint32_t>(kList)) {
@@ -1044,13 +1061,18 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                     const double incl = above + wave_scan_f64_dpp(w);
                     const uint64_t bal = __ballot(lane < n && incl >= target);
                     const int e = bal ? __ffsll(static_cast<unsigned long long>(bal)) - 1 : (n > 0 ? n - 1 : 0);
+                    const double we = readlane_f64(incl, e);
                     if (lane == 0) {
                         ss.bu[5] = ss.skey[e];
                         ss.bu[6] = ss.sidx[e];
+                        ss.bu[3] = static_cast<uint32_t>(e) + 1u;
+                        ss.bd[2] = we;
                     }
                 }
                 __syncthreads();
                 *out = Cut{ss.bu[5], ss.bu[6]};
+                *w_out = ss.bd[2];
+                *n_out = above_n + ss.bu[3];
                 return true;
             }
             if (sh == 0) {
@@ -1065,6 +1087,8 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 }
                 const uint32_t last = keep < cd ? nth_tie(ct, nlo, keep) : (ct.key == nlo ? ct.last : 0xffffffffu);
                 *out = Cut{nlo, last};
+                *w_out = above + static_cast<double>(keep) * w;
+                *n_out = above_n + keep;
                 return true;
             }
             lo = nlo;
@@ -1817,14 +1841,27 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         // ---------------------------- the row itself: top-k, then top-p --
         from_row = true;
         if (mode == kTopK) cut = select_desc(cut, static_cast<uint32_t>(prm.k));
+        bool have_w = false;
         if (prm.top_p) {
-            const double wk = sum_cut(cut, nullptr);
+            // top-p alone: the normaliser is the stream's (its lane sums, same
+            // reference); after a top-k cut, the kept weight
+            double wk = 0.0;
+            if (mode == kTopP && want_lanez) {
+                __syncthreads();        // every wave's share is in ss.wd
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) wk += ss.wd[w];
+            } else {
+                wk = sum_cut(cut, nullptr);
+            }
             Cut pc;
-            if (mass_cut(cut, static_cast<double>(prm.p) * wk, &pc)) cut = pc;
+            if (mass_cut(cut, static_cast<double>(prm.p) * wk, &pc, &W, &n_kept)) {
+                cut = pc;
+                have_w = true;
+            }
         }
 
         // ---- the draw: first index (token order) whose kept prefix exceeds u*W --
-        W = sum_cut(cut, &n_kept);
+        if (!have_w) W = sum_cut(cut, &n_kept);
         double tgt = u * W;
         auto kept = [&](uint32_t k, uint32_t i) { return cut.keep(i, k); };
         uint32_t ilo = 0, ihi = static_cast<uint32_t>(V - 1);
