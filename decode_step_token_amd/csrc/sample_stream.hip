@@ -1837,6 +1837,216 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         }
     }
 
+    // ------------------------------------------- flat top-p rows (row reads) --
+    // The nucleus reaches below theta.  Two passes over the row in the stream's
+    // tile layout: (A) a 1024-bin histogram of weight by depth below the
+    // reference (1/16 octave per bin, the heaviest bin last), from which wave 0
+    // picks the bin where the descending weight reaches p * Z; (B) per-tile
+    // weight of the bins above it (each tile summed by its own wave) and the
+    // entries of that bin gathered into the LDS regions.  The cut inside the
+    // bin is then the mass descent over LDS entries, and the draw scans the
+    // per-tile kept weights and reads the chosen tile once more.
+    if (!fast && mode == kTopP && want_lanez && aligned) {
+        constexpr int kTS = __builtin_ctz(IO::TILE);
+        __syncthreads();                       // every wave's share of Z is in ss.wd
+        double z = 0.0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) z += ss.wd[w];
+        const double ztgt = static_cast<double>(prm.p) * z;
+        // bin index of a value (higher = heavier) and its exponent y, weight 2^y * G
+        auto depth_bin = [&](float x, float* y) -> int {
+            *y = fmaf(x, c32, -Pf);
+            const float dq = -*y * 16.0f;
+            const int bq = dq < 1.0f ? 0 : (dq >= static_cast<float>(kBins - 1) ? kBins - 1 : static_cast<int>(dq));
+            return kBins - 1 - bq;
+        };
+        ss.hcnt[threadIdx.x] = 0u;
+        ss.hmass[threadIdx.x] = 0.0;
+        if (threadIdx.x == 0) { ss.movf = 0u; ss.mtotal = 0u; }
+        __syncthreads();
+        // (A)
+        {
+            uint4 ra[IO::U], rb[IO::U];
+            int tt = wid;
+            if (tt < n_tiles) IO::load(row, V, tt, lane, ra);
+            for (; tt < n_tiles; tt += kWaves) {
+#pragma unroll
+                for (int v = 0; v < IO::U; ++v) rb[v] = ra[v];
+                if (tt + kWaves < n_tiles) IO::load(row, V, tt + kWaves, lane, ra);
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    if (IO::index(tt, lane, q) < static_cast<uint32_t>(V)) {
+                        float y;
+                        const int d = depth_bin(IO::get(rb, q), &y);
+                        atomicAdd(&ss.hcnt[d], 1u);
+                        atomicAdd(&ss.hmass[d], static_cast<double>(__builtin_amdgcn_exp2f(y)));
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (wid == 0) {
+            const BinPick bq = w0_pick_mass(ss.hcnt, ss.hmass, 0.0, ztgt / G);
+            if (lane == 0) ss.bu[2] = static_cast<uint32_t>(bq.d < 0 ? 0 : bq.d);
+        }
+        __syncthreads();
+        const int dpick = static_cast<int>(ss.bu[2]);
+        // (B)
+        {
+            uint4 ra[IO::U], rb[IO::U];
+            uint32_t fill = 0, nabove = 0;
+            const uint32_t rbeg = static_cast<uint32_t>(wid * kRegion);
+            int tt = wid;
+            if (tt < n_tiles) IO::load(row, V, tt, lane, ra);
+            for (; tt < n_tiles; tt += kWaves) {
+#pragma unroll
+                for (int v = 0; v < IO::U; ++v) rb[v] = ra[v];
+                if (tt + kWaves < n_tiles) IO::load(row, V, tt + kWaves, lane, ra);
+                double part = 0.0;
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const float x = IO::get(rb, q);
+                    const uint32_t idx = IO::index(tt, lane, q);
+                    float y;
+                    const int d = depth_bin(x, &y);
+                    const bool valid = idx < static_cast<uint32_t>(V);
+                    const float w = __builtin_amdgcn_exp2f(y);
+                    if (valid && d > dpick) {
+                        part += static_cast<double>(w);
+                        ++nabove;
+                    }
+                    const uint64_t bal = __ballot(valid && d == dpick);
+                    if (bal) {
+                        const uint32_t pos = fill + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u));
+                        if (valid && d == dpick && pos < static_cast<uint32_t>(kRegion)) {
+                            ss.cent[rbeg + pos] = make_uint2(f32_key(x), idx);
+                            ss.cw[rbeg + pos] = static_cast<float>(static_cast<double>(w) * G);
+                        }
+                        fill += static_cast<uint32_t>(__popcll(bal));
+                    }
+                }
+                const double ts = wave_sum_dpp(part);
+                if (lane == 0) ss.tacc[tt] = ts * G;
+            }
+            nabove = readlane_u32(wave_scan_u32_dpp(nabove), kWave - 1);
+            if (lane == 0) {
+                if (fill > static_cast<uint32_t>(kRegion)) atomicOr(&ss.movf, 1u);
+                atomicAdd(&ss.mtotal, nabove);
+            }
+            cnt = fill;
+        }
+        __syncthreads();
+        if (ss.movf == 0u) {
+            // the weight above the bin (per tile, owner-summed) and its count
+            if (wid == 0) {
+                double a = 0.0;
+                for (int i = lane; i < n_tiles; i += kWave) a += ss.tacc[i];
+                a = wave_sum_dpp(a);
+                if (lane == 0) ss.bd[1] = a;
+            }
+            __syncthreads();
+            const double above = ss.bd[1];
+            const uint32_t nabove = ss.mtotal;
+            from_row = false;
+            Cut pc{0u, 0xffffffffu};
+            double wb = 0.0;
+            uint32_t nb = 0;
+            if (!mass_cut(Cut{0u, 0xffffffffu}, ztgt - above, &pc, &wb, &nb)) {
+                // rounding: the target is at or past the bin's end; keep it whole
+                uint32_t lo, hi;
+                key_range(Cut{0u, 0xffffffffu}, &lo, &hi);
+                pc = Cut{lo, 0xffffffffu};
+                wb = sum_cut(pc, &nb);
+            }
+            cut = pc;
+            W = above + wb;
+            n_kept = nabove + nb;
+            // the kept entries of the bin add their weight to their tile
+            each(0u, 0xffffffffu, [&](uint32_t k, uint32_t i, int slot) {
+                if (cut.keep(i, k)) atomicAdd(&ss.tacc[i >> kTS], static_cast<double>(ss.cw[slot]));
+            });
+            __syncthreads();
+            if (wid == 0) {
+                // the tile holding u * W (lane l: tiles l*per ..), then that tile again
+                const int per = (n_tiles + kWave - 1) / kWave;
+                const int tlo = lane * per, thi = tlo + per < n_tiles ? tlo + per : n_tiles;
+                double psum = 0.0;
+                for (int i = tlo; i < thi; ++i) psum += ss.tacc[i];
+                const double incl = wave_scan_f64_dpp(psum);
+                const double tot = readlane_f64(incl, kWave - 1);
+                const double target = u * tot;
+                const uint64_t bal = __ballot(psum > 0.0 && incl > target);
+                const uint64_t nz = __ballot(psum > 0.0);
+                const int owner = bal ? __ffsll(static_cast<unsigned long long>(bal)) - 1
+                                      : (nz ? 63 - __clzll(static_cast<long long>(nz)) : 0);
+                int ts = tlo;
+                double rem = INFINITY;
+                if (lane == owner) {
+                    double cum = incl - psum;
+                    int found = -1, last_nz = tlo;
+                    for (int i = tlo; i < thi; ++i) {
+                        const double v = ss.tacc[i];
+                        if (v > 0.0) last_nz = i;
+                        if (found < 0 && v > 0.0 && cum + v > target) { found = i; rem = target - cum; }
+                        if (found < 0) cum += v;
+                    }
+                    ts = found >= 0 ? found : last_nz;
+                    if (found < 0) rem = INFINITY;
+                }
+                ts = static_cast<int>(readlane_u32(static_cast<uint32_t>(ts), owner));
+                rem = readlane_f64(rem, owner);
+                uint4 rr[IO::U];
+                IO::load(row, V, ts, lane, rr);
+                double run = 0.0;
+                int tok = -1, last_pos = -1;
+#pragma unroll
+                for (int uu = 0; uu < IO::U; ++uu) {
+                    double wv[IO::VEC];
+                    double ps = 0.0;
+                    int my_last = -1;
+#pragma unroll
+                    for (int e = 0; e < IO::VEC; ++e) {
+                        const float x = IO::get(rr, uu * IO::VEC + e);
+                        const uint32_t idx = IO::index(ts, lane, uu * IO::VEC + e);
+                        const bool kp = idx < static_cast<uint32_t>(V) && cut.keep(idx, f32_key(x));
+                        wv[e] = kp ? static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, c32, -Pf))) * G : 0.0;
+                        ps += wv[e];
+                        if (wv[e] > 0.0) my_last = static_cast<int>(idx);
+                    }
+                    const double pin = wave_scan_f64_dpp(ps);
+                    const double tsum = readlane_f64(pin, kWave - 1);
+                    const uint64_t lastb = __ballot(my_last >= 0);
+                    if (lastb)
+                        last_pos = static_cast<int>(readlane_u32(static_cast<uint32_t>(my_last),
+                                                                 63 - __clzll(static_cast<long long>(lastb))));
+                    if (tok < 0 && run + tsum > rem) {
+                        const uint64_t ob = __ballot(ps > 0.0 && run + pin > rem);
+                        if (ob) {
+                            const int own = __ffsll(static_cast<unsigned long long>(ob)) - 1;
+                            int mine = -1;
+                            bool done_l = false;
+                            double cum = run + (pin - ps);
+#pragma unroll
+                            for (int e = 0; e < IO::VEC; ++e) {
+                                cum += wv[e];
+                                if (!done_l && wv[e] > 0.0) mine = static_cast<int>(IO::index(ts, lane, uu * IO::VEC + e));
+                                if (wv[e] > 0.0 && cum > rem) done_l = true;
+                            }
+                            tok = static_cast<int>(readlane_u32(static_cast<uint32_t>(mine), own));
+                        }
+                    }
+                    run += tsum;
+                }
+                if (tok < 0) tok = last_pos;
+                if (lane == 0) ss.bu[7] = static_cast<uint32_t>(tok);
+            }
+            __syncthreads();
+            token = ss.bu[7];
+            fast = true;
+        }
+    }
+
     if (!fast) {
         // ---------------------------- the row itself: top-k, then top-p --
         from_row = true;

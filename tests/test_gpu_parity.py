@@ -168,6 +168,17 @@ def test_flat_rows_fall_back_to_exact():
     _check(w)
 
 
+def test_c3_flat_top_p_rows():
+    """c3 logits with a high temperature and top-p only: the nucleus of many
+    rows reaches below the candidate threshold, so they take the two-pass
+    flat-row path (depth histogram, then the boundary bin in LDS)."""
+    w = wl.c3()
+    w.temperature[:] = np.float32(1.5)
+    w.top_k[:] = -1
+    w.top_p[:] = np.where(np.arange(w.B) % 2 == 0, 0.95, 0.99).astype(np.float32)
+    _check(w, probs_rows=set(range(0, 256, 17)))
+
+
 def test_c2_full():
     _check(wl.c2(), probs_rows=set(range(0, 256, 17)))
 
