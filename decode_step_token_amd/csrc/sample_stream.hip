@@ -52,6 +52,7 @@ constexpr int kRegion = 512;               // candidate entries per wave
 constexpr int kCap = kWaves * kRegion;     // 8192
 constexpr int kMaxTiles = 512;
 constexpr int kList = 64;
+constexpr int kTopKCands = 4096;          // top-k rows: candidate count the threshold aims below
 constexpr int kTopPTarget = 1500;          // aimed-at candidate count for top-p rows
 constexpr int kBins = 1024;                // candidate histograms: 16 bins per lane of wave 0
 constexpr int kBinsPerLane = kBins / kWave;
@@ -674,7 +675,14 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         const int first_elems = V < kWaves * IO::TILE ? V : kWaves * IO::TILE;
         uint32_t j;
         if (mode == kTopK) {
-            j = static_cast<uint32_t>(prm.k < kBlock ? prm.k : kBlock);
+            // j = k makes the top-k set always fit (j maxima are j distinct
+            // logits >= theta); a large k would then keep far more candidates
+            // than the regions hold, so j stops at about kTopKCands expected
+            // candidates (the k-th largest is then almost always above theta;
+            // when not, the row is finished from the row itself)
+            const long long jcap = (static_cast<long long>(kTopKCands) * first_elems + V - 1) / V;
+            const long long jc = jcap < 64 ? 64 : (jcap > kBlock ? kBlock : jcap);
+            j = static_cast<uint32_t>(prm.k < jc ? prm.k : jc);
         } else {
             const long long want = (static_cast<long long>(kTopPTarget) * first_elems + V - 1) / V;
             j = static_cast<uint32_t>(want < 64 ? 64 : (want > kBlock ? kBlock : want));

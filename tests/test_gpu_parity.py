@@ -179,6 +179,20 @@ def test_c3_flat_top_p_rows():
     _check(w, probs_rows=set(range(0, 256, 17)))
 
 
+def test_large_top_k_rows():
+    """Top-k above the list size at full vocabulary: the threshold aims at a
+    bounded candidate count (k = 3000 keeps thousands), the pass-driven
+    descent finishes the rows; with and without top-p."""
+    w = wl.c3()
+    sel = np.arange(32)
+    w = wl.Workload("c3_large_k", w.dtype, w.logits[sel].copy(), w.temperature[sel].copy(),
+                    np.array([100, 500, 1000, 3000] * 8, dtype=np.int32),
+                    np.array([1.0] * 16 + [0.9] * 16, dtype=np.float32),
+                    w.uid[sel].copy(), w.step, w.pool[sel].copy(), np.arange(32, dtype=np.int64),
+                    w.cols[sel].copy())
+    _check(w, probs_rows={0, 5, 30})
+
+
 def test_c2_full():
     _check(wl.c2(), probs_rows=set(range(0, 256, 17)))
 
