@@ -1720,6 +1720,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 top_ext = false;
             }
             int route = 0;           // 0 general, 1 S, 2 P, 3 finish from the row
+            double ptgt = 0.0;       // top-p rows: p * Z
             BlockPick bp{};
             // the softmax normaliser of a top-p row (same value wherever it is used)
             auto row_z = [&]() -> double {
@@ -1729,7 +1730,8 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 bp = block_pick(false, static_cast<uint32_t>(prm.k), 0.0);
                 if (bp.d >= 0 && bp.above_c + bp.cnt <= static_cast<uint32_t>(kList)) route = 1;
             } else if (mode == kTopP) {
-                bp = block_pick(true, 0u, static_cast<double>(prm.p) * row_z());
+                ptgt = static_cast<double>(prm.p) * row_z();
+                bp = block_pick(true, 0u, ptgt);
                 if (bp.d < 0) route = 3;
                 else if (bp.above_c + bp.cnt <= static_cast<uint32_t>(kList)) route = 1;   // the whole nucleus listed
                 else if (bp.cnt <= static_cast<uint32_t>(kList)) route = 2;
@@ -1752,8 +1754,8 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                     const int k = mode == kTopK ? prm.k : n;
                     int e = k - 1;
                     if (prm.top_p) {
-                        const double target_p = static_cast<double>(prm.p) *
-                            (mode == kTopK ? readlane_f64(incl, k - 1) : row_z());
+                        const double target_p = mode == kTopK
+                            ? static_cast<double>(prm.p) * readlane_f64(incl, k - 1) : ptgt;
                         const uint64_t bal = __ballot(lane < k && incl >= target_p);
                         if (bal) e = __ffsll(static_cast<unsigned long long>(bal)) - 1;
                     }
@@ -1787,7 +1789,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                     const bool in = lane < n;
                     const double w = in ? static_cast<double>(ss.sw[lane]) : 0.0;
                     const double incl = wave_scan_f64_dpp(w);
-                    const double target_p = static_cast<double>(prm.p) * row_z();
+                    const double target_p = ptgt;
                     const uint64_t bal = __ballot(in && bp.above_m + incl >= target_p);
                     const int e = bal ? __ffsll(static_cast<unsigned long long>(bal)) - 1 : n - 1;
                     if (in && lane <= e)
