@@ -43,10 +43,14 @@ def eprint(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# the files the sample_batch kernel is compiled from
+KERNEL_SOURCES = ("device_common.hpp", "kernels.hpp", "sample_stream.hip")
+
+
 def kernel_sources_digest() -> str:
     csrc = os.path.join(ROOT, "decode_step_token_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -155,6 +159,10 @@ def main():
                     help="record counter-measured bytes per launch in profiles/traffic.json")
     ap.add_argument("--traffic-command", default="",
                     help="with --write-traffic: the profiling command, stored with the figures")
+    ap.add_argument("--workload", choices=("c3", "c4loop"), default="c3",
+                    help="c3: the headline sampler step (default); c4loop: the overlapped "
+                         "decode loop gather -> sample -> write at B=512 V=152064 bf16, plus "
+                         "the input gather alone")
     args = ap.parse_args()
 
     if args.write_traffic:
@@ -166,6 +174,10 @@ def main():
         print(f"bench.py: this sampler runs on one GPU; --gpus {args.gpus} is not supported "
               f"(rows are independent: shard the batch, one process per GPU)", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "c4loop":
+        bench_c4_loop(args)
+        return
 
     import numpy as np
     import torch
@@ -281,6 +293,129 @@ def main():
                      "kernel": "sample_batch", "kernel_avg_us": avg_kernel_ms * 1e3,
                      "alg_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+GATHER_BYTES_PER_ENTRY = 8 + 8 + 4 + 4     # row, position read; pool id read; id written
+
+
+def bench_c4_loop(args):
+    """The scheduler's overlapped decode loop on the c4 workload: per step
+    gather_tokens (input ids at device_len - 1) -> sample_batch -> write_tokens
+    (pool at device_len, host copy); step s waits for step s-1's ticket after
+    enqueuing step s.  Logits of a few distinct steps are resident and used in
+    rotation while the step counter advances.  Also times gather_tokens alone
+    for the decode batch and for a prefill-sized input tuple."""
+    import numpy as np
+    import torch
+
+    import decode_step_token_amd as dst
+    import workloads as wl
+
+    nbuf = max(1, args.buffers)
+    eprint(f"bench: generating the B=512 V=152064 bf16 decode-loop workload ({nbuf} steps of logits)")
+    w = wl.c4(0)
+    B, V = w.B, w.V
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bufs = [torch.from_numpy(wl.c4_logits(i).view(np.int16)).to(dev) for i in range(nbuf)]
+    T = torch.from_numpy(w.temperature).to(dev)
+    k = torch.from_numpy(w.top_k).to(dev)
+    p = torch.from_numpy(w.top_p).to(dev)
+    uid = torch.from_numpy(w.uid).to(dev)
+    pool = torch.from_numpy(w.pool.copy()).to(dev)
+    rows = torch.from_numpy(w.rows).to(dev)
+    pos0 = w.meta["pos0"]
+    total = args.warmup + args.steps
+    if int(pos0.max()) + total > w.pool.shape[1]:
+        raise SystemExit(f"bench.py: {total} steps run past the pool's {w.pool.shape[1]} columns")
+    in_pos = [torch.from_numpy(pos0 + s - 1).to(dev) for s in range(total)]
+    out_pos = [torch.from_numpy(pos0 + s).to(dev) for s in range(total)]
+    ids = torch.empty(B, dtype=torch.int32, device=dev)
+    tokens = torch.empty(B, dtype=torch.int32, device=dev)
+    host_ring = [torch.empty(B, dtype=torch.int32).pin_memory() for _ in range(2)]
+    sampler = dst.Sampler(0, B, V, "bf16", w.seed)
+    stream = torch.cuda.current_stream()
+
+    def step(s):
+        sampler.gather(pool, rows, in_pos[s], ids_out=ids, stream=stream)
+        sampler.sample(bufs[s % nbuf], temperature=T, top_k=k, top_p=p, uid=uid, step=s,
+                       tokens_out=tokens, stream=stream)
+        return sampler.write(pool, rows, out_pos[s], tokens, host_ring[s % 2], stream)
+
+    def loop(first, count):
+        prev = None
+        for s in range(first, first + count):
+            t = step(s)
+            if prev is not None:
+                sampler.wait(prev)
+            prev = t
+        if prev is not None:
+            sampler.wait(prev)
+
+    eprint(f"bench: warmup {args.warmup} steps")
+    loop(0, args.warmup)
+    torch.cuda.synchronize()
+    eprint(f"bench: timing {args.steps} loop steps")
+    t0 = time.perf_counter()
+    loop(args.warmup, args.steps)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    def time_gather(r, c, reps):
+        out = torch.empty(r.numel(), dtype=torch.int32, device=dev)
+        for _ in range(3):
+            sampler.gather(pool_big, r, c, ids_out=out, stream=stream)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        # hold the stream in a spin kernel while the launches are enqueued, so
+        # that they run back to back rather than at the host's launch rate
+        torch.cuda._sleep(int(reps * 20e3))
+        ev0.record(stream)
+        for _ in range(reps):
+            sampler.gather(pool_big, r, c, ids_out=out, stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / reps
+        n = r.numel()
+        gbs = n * GATHER_BYTES_PER_ENTRY / (us * 1e-6) / 1e9
+        return {"entries": n, "avg_us": us, "achieved_GBs": gbs, "frac": gbs / PEAK_HBM_GBS}
+
+    # a prefill-sized input tuple: every request of the batch runs 1024
+    # positions of its row (spans of neighbouring columns)
+    pool_big = pool
+    span = 1024
+    pr = torch.arange(B, device=dev, dtype=torch.int64).repeat_interleave(span)
+    pc = torch.arange(span, device=dev, dtype=torch.int64).repeat(B)
+    g_decode = time_gather(rows, in_pos[0], args.steps)
+    g_prefill = time_gather(pr, pc, args.steps)
+    sampler.check()
+    sampler.close()
+    eprint(f"bench: {ms_per_step * 1e3:.1f} us/loop step; gather decode {g_decode['avg_us']:.2f} us, "
+           f"prefill {g_prefill['entries']} entries {g_prefill['avg_us']:.2f} us "
+           f"({g_prefill['achieved_GBs']:.0f} GB/s)")
+    out = {
+        "metric": "decode-loop steps: sampled rows/sec at B=512, V=152064 (gather + sample + write)",
+        "value": B / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "c4 decode loop: B=512 V=152064 bf16 N(0,2.5) logits, c3 parameter "
+                               "mix, token pool [512,4096] from per-request positions U[1,2048]; "
+                               "gather -> sample -> write, step s waits for step s-1's host copy",
+                   "B": B, "V": V, "logits_dtype": "bf16", "input_buffers": nbuf,
+                   "parallelism": "single GPU"},
+        "gather_tokens": {"bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                          "bytes_per_entry": GATHER_BYTES_PER_ENTRY,
+                          "decode": g_decode, "prefill": g_prefill},
     }
     print(json.dumps(out), flush=True)
 

@@ -27,8 +27,9 @@ SAMPLER_DEBUG_FORCE_EXACT = 1
 STATUS = {0: "SAMPLER_OK", -1: "SAMPLER_EINVAL", -2: "SAMPLER_ENOMEM", -3: "SAMPLER_EHIP",
           -4: "SAMPLER_ENOTPINNED", -5: "SAMPLER_EDEVICE", -6: "SAMPLER_ETICKET"}
 
-EXPORTS = ("sampler_create", "sampler_destroy", "sample_batch", "write_tokens", "sampler_wait",
-           "sampler_query", "sampler_check", "sampler_strerror", "sampler_last_error")
+EXPORTS = ("sampler_create", "sampler_destroy", "sample_batch", "write_tokens", "gather_tokens",
+           "sampler_wait", "sampler_query", "sampler_check", "sampler_strerror",
+           "sampler_last_error")
 
 
 class SamplerError(RuntimeError):
@@ -60,6 +61,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sampler_destroy.argtypes = [P]
     lib.sample_batch.argtypes = [P, P, P, I64, I32, P, P, P, P, U64, P, ctypes.POINTER(SamplerDebug)]
     lib.write_tokens.argtypes = [P, P, P, I64, I64, P, P, P, I32, P, ctypes.POINTER(U64)]
+    lib.gather_tokens.argtypes = [P, P, P, I64, I64, P, P, I64, P]
     lib.sampler_wait.argtypes = [P, U64]
     lib.sampler_query.argtypes = [P, U64]
     lib.sampler_check.argtypes = [P]
@@ -68,7 +70,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sampler_last_error.argtypes = [P]
     lib.sampler_last_error.restype = ctypes.c_char_p
     for name in ("sampler_create", "sampler_destroy", "sample_batch", "write_tokens",
-                 "sampler_wait", "sampler_query", "sampler_check"):
+                 "gather_tokens", "sampler_wait", "sampler_query", "sampler_check"):
         getattr(lib, name).restype = INT
     _lib = lib
     return lib
@@ -183,6 +185,26 @@ def write_tokens(handle, token_pool: torch.Tensor, rows: torch.Tensor, cols: tor
     return ticket.value
 
 
+def gather_tokens(handle, token_pool: torch.Tensor, rows: torch.Tensor, positions: torch.Tensor,
+                  ids_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``token_pool[rows, positions]`` on the device (the step's input ids)."""
+    if token_pool.dim() != 2 or not token_pool.is_contiguous():
+        raise ValueError("token_pool must be a contiguous [R, C] tensor")
+    dev = token_pool.device
+    n = rows.numel()
+    if positions.numel() != n:
+        raise ValueError("rows and positions must have the same length")
+    if ids_out is None:
+        ids_out = torch.empty(n, dtype=torch.int32, device=dev)
+    code = load().gather_tokens(
+        handle, _stream(stream), _ptr(token_pool, "token_pool", torch.int32, None, dev),
+        token_pool.shape[0], token_pool.shape[1],
+        _ptr(rows, "rows", torch.int64, n, dev), _ptr(positions, "positions", torch.int64, n, dev),
+        n, _ptr(ids_out, "ids_out", torch.int32, n, dev))
+    _check(code, "gather_tokens", handle)
+    return ids_out
+
+
 def sampler_wait(handle, ticket: int) -> None:
     _check(load().sampler_wait(handle, int(ticket)), "sampler_wait", handle)
 
@@ -213,6 +235,9 @@ class Sampler:
 
     def write(self, token_pool, rows, cols, tokens, host_out=None, stream=None) -> int:
         return write_tokens(self.handle, token_pool, rows, cols, tokens, host_out, stream)
+
+    def gather(self, token_pool, rows, positions, ids_out=None, stream=None) -> torch.Tensor:
+        return gather_tokens(self.handle, token_pool, rows, positions, ids_out, stream)
 
     def wait(self, ticket: int) -> None:
         sampler_wait(self.handle, ticket)

@@ -49,10 +49,21 @@ struct WriteArgs {
     int32_t* host;             // device address of the pinned host copy, or null
 };
 
+struct GatherArgs {
+    const int32_t* pool;
+    int64_t pool_rows, pool_cols;
+    const int64_t* rows;
+    const int64_t* positions;
+    int64_t n;
+    int32_t* ids_out;
+    uint32_t* status;          // mapped pinned host word; set to 1 on a bad (row, position)
+};
+
 hipError_t launch_argmax(const ArgmaxArgs& args, int dtype, hipStream_t stream);
 void argmax_plan(int B, int V, int dtype, int* chunks, int* chunk_len);
 hipError_t launch_sample_exact(const SampleArgs& args, int dtype, hipStream_t stream);
 hipError_t launch_sample_stream(const SampleArgs& args, int dtype, hipStream_t stream);
 hipError_t launch_write_tokens(const WriteArgs& args, hipStream_t stream);
+hipError_t launch_gather_tokens(const GatherArgs& args, hipStream_t stream);
 
 }  // namespace dst

@@ -5,7 +5,8 @@
 // done on the device; write_tokens is the scheduler's token-pool write-back
 // plus forward_batch's non-blocking host copy and completion event ("The
 // scheduler skeleton and the offline interface", section "_forward"; "The
-// engine and the sampler", section "forward_batch").
+// engine and the sampler", section "forward_batch"); gather_tokens is
+// _forward's input gather from the same pool.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -19,6 +20,8 @@
 namespace {
 
 constexpr int kRing = 256;
+// one thread per gathered entry: a dispatch holds fewer than 2^32 work-items
+constexpr int64_t kMaxGather = INT32_MAX;
 // all-greedy batches with at least this many rows fill the GPU with one
 // workgroup per row and take the single-pass kernel; smaller ones split rows
 constexpr int kStreamGreedyMinRows = 256;
@@ -236,6 +239,23 @@ int write_tokens(dst_sampler* s, void* stream, int32_t* token_pool, int64_t pool
     s->issued = ticket;
     s->ring_ticket[ticket % kRing] = ticket;
     if (ticket_out) *ticket_out = ticket;
+    return SAMPLER_OK;
+}
+
+int gather_tokens(dst_sampler* s, void* stream, const int32_t* token_pool, int64_t pool_rows,
+                  int64_t pool_cols, const int64_t* rows, const int64_t* positions, int64_t n,
+                  int32_t* ids_out) {
+    if (!s) return SAMPLER_EINVAL;
+    if (n < 0) return fail(s, SAMPLER_EINVAL, "gather_tokens: n < 0");
+    if (n > kMaxGather) return fail(s, SAMPLER_EINVAL, "gather_tokens: n too large");
+    if (n > 0 && (!token_pool || !rows || !positions || !ids_out))
+        return fail(s, SAMPLER_EINVAL, "gather_tokens: null pointer");
+    if (pool_rows < 1 || pool_cols < 1) return fail(s, SAMPLER_EINVAL, "gather_tokens: empty pool");
+    if (n == 0) return SAMPLER_OK;
+    DeviceGuard g(s->device);
+    dst::GatherArgs a{token_pool, pool_rows, pool_cols, rows, positions, n, ids_out, s->status_dev};
+    const hipError_t e = dst::launch_gather_tokens(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(s, SAMPLER_EHIP, "gather_tokens: launch", e);
     return SAMPLER_OK;
 }
 

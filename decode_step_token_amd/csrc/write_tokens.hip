@@ -1,4 +1,4 @@
-// Token-pool write-back.
+// Token-pool write-back and input gather.
 //
 // "The scheduler skeleton and the offline interface", section "Preparing a
 // batch": _make_write_tuple gives each request (row = table_idx, col =
@@ -12,6 +12,15 @@
 // The host copy of forward_batch is the same kernel: each thread also stores
 // its token into the caller's pinned buffer through its device mapping, with
 // system scope, so the completion event covers it.
+//
+// The input gather is the other side of the same pool: the step's input ids
+// are token_pool[input_tuple] with input_tuple = (row, position) over each
+// request's positions [cached_len, device_len), packed request after request
+// (same page, sections "Preparing a batch" and "_forward").  One thread per
+// packed entry; neighbouring entries of one request read neighbouring pool
+// cells, so prefill spans coalesce and a decode batch (one entry per
+// request) is one scattered 4-byte read per lane.  An out-of-range entry
+// yields id -1 and raises the status word.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -36,7 +45,29 @@ __global__ __launch_bounds__(kWriteBlock) void write_tokens_kernel(WriteArgs a) 
     if (a.host) __hip_atomic_store(a.host + b, tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+constexpr int kGatherBlock = 256;
+
+__global__ __launch_bounds__(kGatherBlock) void gather_tokens_kernel(GatherArgs a) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kGatherBlock + threadIdx.x;
+    if (i >= a.n) return;
+    const int64_t r = a.rows[i];
+    const int64_t c = a.positions[i];
+    int32_t id = -1;
+    if (r >= 0 && r < a.pool_rows && c >= 0 && c < a.pool_cols) {
+        id = a.pool[r * a.pool_cols + c];
+    } else {
+        *reinterpret_cast<volatile uint32_t*>(a.status) = 1u;
+    }
+    a.ids_out[i] = id;
+}
+
 }  // namespace
+
+hipError_t launch_gather_tokens(const GatherArgs& args, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>((args.n + kGatherBlock - 1) / kGatherBlock));
+    hipLaunchKernelGGL(gather_tokens_kernel, grid, dim3(kGatherBlock), 0, stream, args);
+    return hipGetLastError();
+}
 
 hipError_t launch_write_tokens(const WriteArgs& args, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>((args.B + kWriteBlock - 1) / kWriteBlock));

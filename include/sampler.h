@@ -15,7 +15,8 @@
  *       device copy, a non-blocking host copy and a completion event;
  *   "The scheduler skeleton and the offline interface", sections "Preparing a
  *       batch" (_make_write_tuple) and "_forward" -- token_pool[row, col] =
- *       token, a column of -1 lands in the last column.
+ *       token, a column of -1 lands in the last column; the step's input ids
+ *       are gathered from the same pool at (row, position).
  *
  * Conventions for every entry point:
  *   - Return value: 0 (SAMPLER_OK) or a negative SAMPLER_E* code.  No C++
@@ -27,8 +28,8 @@
  *     workspace allocated once in sampler_create, a small pinned status word
  *     and a ring of completion events.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
- *     sample_batch and write_tokens only enqueue work on `stream`: they never
- *     allocate and never wait for the device.
+ *     sample_batch, write_tokens and gather_tokens only enqueue work on
+ *     `stream`: they never allocate and never wait for the device.
  *   - Argument errors that the host can see are reported synchronously and
  *     nothing is enqueued.  Parameter *values* in device memory are never
  *     errors: they are clamped on the device as Sampler.prepare clamps them.
@@ -61,7 +62,7 @@ enum sampler_status {
     SAMPLER_ENOMEM = -2,      /* workspace or event allocation failed               */
     SAMPLER_EHIP = -3,        /* a HIP runtime call or kernel launch failed         */
     SAMPLER_ENOTPINNED = -4,  /* host_pinned_out is not page-locked host memory     */
-    SAMPLER_EDEVICE = -5,     /* a device-side bounds check fired (see write_tokens) */
+    SAMPLER_EDEVICE = -5,     /* a device-side bounds check fired (write/gather)     */
     SAMPLER_ETICKET = -6      /* unknown ticket                                      */
 };
 
@@ -168,6 +169,30 @@ DST_API int write_tokens(dst_sampler* s, void* stream, int32_t* token_pool, int6
                  int64_t pool_cols, const int64_t* rows, const int64_t* cols,
                  const int32_t* tokens, int32_t B, int32_t* host_pinned_out,
                  uint64_t* ticket_out);
+
+/*
+ * gather_tokens -- ids_out[i] = token_pool[rows[i], positions[i]]: the step's
+ * input ids, gathered on the device so the host never sees token values
+ * ("The scheduler skeleton and the offline interface", section "Preparing a
+ * batch": input_tuple = (row, position) over each request's positions
+ * [cached_len, device_len), packed one request after another; section
+ * "_forward": input_ids = token_pool[input_tuple]).
+ *   token_pool  dev [pool_rows, pool_cols] int32, row-major (read only).
+ *   rows, positions  dev [n] int64, one (pool row, column) per input token.
+ *               A decode batch has one entry per request, at device_len - 1.
+ *               Indices are taken as given (no wrap of negative values): an
+ *               entry outside [0, pool_rows) x [0, pool_cols) yields id -1 and
+ *               raises the handle's device flag (SAMPLER_EDEVICE from the next
+ *               sampler_wait / sampler_check).
+ *   n           0 <= n <= INT32_MAX; n == 0 enqueues nothing.
+ *   ids_out     dev [n] int32, written by the kernel; caller-owned.
+ * Ordered on `stream` like every call: a gather after a write_tokens on the
+ * same stream sees its tokens.  No ticket (no host side effect).
+ * Errors: SAMPLER_EINVAL (synchronous); SAMPLER_EHIP.
+ */
+DST_API int gather_tokens(dst_sampler* s, void* stream, const int32_t* token_pool,
+                          int64_t pool_rows, int64_t pool_cols, const int64_t* rows,
+                          const int64_t* positions, int64_t n, int32_t* ids_out);
 
 /*
  * sampler_wait -- block until the ticket's work (and its host copy) is done:

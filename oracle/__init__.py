@@ -14,14 +14,17 @@ Pins (each in ``tests/test_oracle_pins.py``):
   against ``heapq.nsmallest``, the draw against ``numpy.searchsorted`` and a
   brute-force sweep of ``u``, the filter-order counterexample.
 * ``write_tokens``: NumPy fancy-index assignment.
+* ``gather_tokens`` / ``input_tuple``: NumPy fancy indexing, a write-then-gather
+  round trip, and the packed positions of a hand-worked prefill + decode batch.
 """
 from .philox import philox4x64, request_uniform, request_word, uniform24
 from .sampler_ref import (CUT_BAND, DRAW_BAND, MIN_P, MIN_T, RowParams, RowResult,
-                          descending_order, filter_sorted, inverse_cdf, row_params,
-                          sample_batch, sample_row, widen_logits, write_tokens)
+                          descending_order, filter_sorted, gather_tokens, input_tuple,
+                          inverse_cdf, row_params, sample_batch, sample_row, widen_logits,
+                          write_tokens)
 
 __all__ = [
     "philox4x64", "request_uniform", "request_word", "uniform24", "CUT_BAND", "DRAW_BAND",
     "MIN_P", "MIN_T", "RowParams", "RowResult", "descending_order", "filter_sorted",
-    "inverse_cdf", "row_params", "sample_batch", "sample_row", "widen_logits", "write_tokens",
+    "gather_tokens", "input_tuple", "inverse_cdf", "row_params", "sample_batch", "sample_row", "widen_logits", "write_tokens",
 ]

@@ -241,3 +241,34 @@ def write_tokens(pool: np.ndarray, rows: np.ndarray, cols: np.ndarray, tokens: n
         else:
             bad = True
     return out, np.asarray(tokens, dtype=np.int32).copy(), bad
+
+
+def gather_tokens(pool: np.ndarray, rows: np.ndarray, positions: np.ndarray):
+    """``token_pool[rows, positions]``: the step's input ids ("The scheduler
+    skeleton and the offline interface", sections "Preparing a batch" and
+    "_forward").  Indices are used as given; an entry outside the pool gives
+    -1 and is reported.
+
+    Returns (ids int32 [n], out_of_range flag)."""
+    R, C = pool.shape
+    ids = np.full(len(rows), -1, dtype=np.int32)
+    bad = False
+    for i in range(len(rows)):
+        r, c = int(rows[i]), int(positions[i])
+        if 0 <= r < R and 0 <= c < C:
+            ids[i] = pool[r, c]
+        else:
+            bad = True
+    return ids, bad
+
+
+def input_tuple(table_idx, cached_len, device_len):
+    """(rows, positions) of one batch: every request contributes its positions
+    [cached_len, device_len) in order, request after request (same page,
+    section "Preparing a batch")."""
+    rows, pos = [], []
+    for r, lo, hi in zip(table_idx, cached_len, device_len):
+        for c in range(int(lo), int(hi)):
+            rows.append(int(r))
+            pos.append(c)
+    return np.asarray(rows, dtype=np.int64), np.asarray(pos, dtype=np.int64)

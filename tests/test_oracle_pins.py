@@ -18,6 +18,7 @@ import scipy.stats
 import oracle
 from oracle import (filter_sorted, inverse_cdf, philox4x64, request_uniform, request_word,
                     row_params, sample_batch, sample_row, widen_logits, write_tokens)
+from oracle import gather_tokens, input_tuple
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 M64 = (1 << 64) - 1
@@ -338,6 +339,73 @@ def test_write_tokens_matches_fancy_index():
     assert bad
     _, _, bad = write_tokens(pool, np.array([0]), np.array([-2]), np.array([1]))
     assert bad
+
+
+# ------------------------------------------------------- input gather ---
+
+def test_gather_tokens_matches_fancy_index():
+    rng = np.random.default_rng(9)
+    R, C, n = 12, 50, 300
+    pool = rng.integers(-5, 1 << 20, (R, C)).astype(np.int32)
+    rows = rng.integers(0, R, n).astype(np.int64)      # repeats allowed (prefill spans)
+    pos = rng.integers(0, C, n).astype(np.int64)
+    ids, bad = gather_tokens(pool, rows, pos)
+    assert ids.dtype == np.int32 and np.array_equal(ids, pool[rows, pos]) and not bad
+    ids, bad = gather_tokens(pool, np.zeros(0, np.int64), np.zeros(0, np.int64))
+    assert ids.shape == (0,) and not bad
+
+
+def test_gather_tokens_out_of_range_is_reported_not_wrapped():
+    pool = np.arange(12, dtype=np.int32).reshape(3, 4)
+    for r, c in ((3, 0), (0, 4), (-1, 0), (0, -1), (1 << 40, 0)):
+        ids, bad = gather_tokens(pool, np.array([1, r]), np.array([2, c]))
+        assert bad and ids[0] == 6 and ids[1] == -1, (r, c)
+
+
+def test_write_then_gather_round_trip():
+    """The next step's input at (row, device_len) is the token just written
+    there; a column of -1 was written to the last column."""
+    rng = np.random.default_rng(10)
+    R, C, B = 32, 64, 20
+    pool = rng.integers(0, 1000, (R, C)).astype(np.int32)
+    rows = rng.permutation(R)[:B].astype(np.int64)
+    cols = rng.integers(0, C, B).astype(np.int64)
+    cols[::5] = -1
+    toks = rng.integers(1000, 2000, B).astype(np.int32)
+    new, _, _ = write_tokens(pool, rows, cols, toks)
+    ids, bad = gather_tokens(new, rows, np.where(cols == -1, C - 1, cols))
+    assert np.array_equal(ids, toks) and not bad
+
+
+def test_input_tuple_hand_worked_batch():
+    """A prefill of 4 tokens, a decode at position 7 and a one-token chunk at
+    position 2, packed request after request."""
+    rows, pos = input_tuple([3, 0, 5], [0, 7, 2], [4, 8, 3])
+    assert rows.tolist() == [3, 3, 3, 3, 0, 5] and pos.tolist() == [0, 1, 2, 3, 7, 2]
+    rows, pos = input_tuple([1], [5], [5])                 # nothing to run
+    assert rows.shape == (0,) and pos.shape == (0,)
+
+
+def test_gather_equals_concatenated_request_slices():
+    """Driving the engine by hand ("The engine and the sampler"), the batch's
+    input is the concatenation of every request's ids[cached_len:device_len];
+    with each request's ids stored in its pool row, gathering the input tuple
+    gives the same array."""
+    rng = np.random.default_rng(11)
+    R, C = 8, 96
+    pool = np.full((R, C), -9, dtype=np.int32)
+    table_idx = rng.permutation(R)[:5]
+    reqs = []
+    for t in table_idx:
+        L = int(rng.integers(1, C))
+        ids = rng.integers(0, 50000, L).astype(np.int32)
+        pool[t, :L] = ids
+        lo = int(rng.integers(0, L))
+        reqs.append((t, lo, L, ids))
+    rows, pos = input_tuple([r[0] for r in reqs], [r[1] for r in reqs], [r[2] for r in reqs])
+    got, bad = gather_tokens(pool, rows, pos)
+    want = np.concatenate([ids[lo:hi] for _, lo, hi, ids in reqs])
+    assert np.array_equal(got, want) and not bad
 
 
 def test_module_header_marks_test_infrastructure():

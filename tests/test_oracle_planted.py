@@ -75,6 +75,38 @@ def _write_minus_one_to_first(pool, rows, cols, tokens):
 
 
 _real_write = sr.write_tokens
+_real_gather = sr.gather_tokens
+_real_input_tuple = sr.input_tuple
+
+
+def _gather_transposed(pool, rows, positions):
+    # operands swapped: reads pool[position, row] (square pools hide it)
+    R, C = pool.shape
+    ids = np.full(len(rows), -1, dtype=np.int32)
+    bad = False
+    for i in range(len(rows)):
+        r, c = int(positions[i]), int(rows[i])
+        if 0 <= r < R and 0 <= c < C:
+            ids[i] = pool[r, c]
+        else:
+            bad = True
+    return ids, bad
+
+
+def _gather_wraps_negative(pool, rows, positions):
+    # NumPy-style wrap of negative indices instead of a reported miss
+    R, C = pool.shape
+    r = np.asarray(rows, dtype=np.int64)
+    c = np.asarray(positions, dtype=np.int64)
+    ok = (r >= -R) & (r < R) & (c >= -C) & (c < C)
+    ids = np.full(len(r), -1, dtype=np.int32)
+    ids[ok] = pool[r[ok], c[ok]]
+    return ids, bool((~ok).any())
+
+
+def _input_tuple_inclusive(table_idx, cached_len, device_len):
+    # off by one: runs [cached_len, device_len]
+    return _real_input_tuple(table_idx, cached_len, [int(d) + 1 for d in device_len])
 
 
 def _run_pins(names):
@@ -100,13 +132,18 @@ PLANTS = [
     ("descending_order", _last_index_ties, ["test_topk_set_matches_heapq_with_index_ties"]),
     ("inverse_cdf", _draw_ge, ["test_draw_measure_brute_force"]),
     ("write_tokens", _write_minus_one_to_first, ["test_write_tokens_matches_fancy_index"]),
+    ("gather_tokens", _gather_transposed, ["test_gather_tokens_matches_fancy_index"]),
+    ("gather_tokens", _gather_wraps_negative,
+     ["test_gather_tokens_out_of_range_is_reported_not_wrapped"]),
+    ("input_tuple", _input_tuple_inclusive, ["test_input_tuple_hand_worked_batch"]),
 ]
 
 
 @pytest.mark.parametrize("attr,bad,pin_names", PLANTS, ids=[p[1].__name__ for p in PLANTS])
 def test_planted_sampler_mistake_is_caught(monkeypatch, attr, bad, pin_names):
     monkeypatch.setattr(sr, attr, bad)
-    for mod_name in ("filter_sorted", "inverse_cdf", "write_tokens"):
+    for mod_name in ("filter_sorted", "inverse_cdf", "write_tokens", "gather_tokens",
+                     "input_tuple"):
         if attr == mod_name:
             monkeypatch.setattr(pins, mod_name, bad)
     with pytest.raises(Exception):    # a failed assertion, or the oracle breaking outright

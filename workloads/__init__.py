@@ -228,6 +228,46 @@ def c4(step: int = 0, half_greedy: bool = False) -> Workload:
 
 CONFIGS = {"c0": c0, "c1": c1, "c2": c2, "c3": c3, "c4": c4}
 
+LOOP_B, LOOP_V, LOOP_POOL = 64, 4096, (64, 256)
+
+
+def loop_small_logits(step: int) -> np.ndarray:
+    rng = np.random.default_rng([1104, step])
+    x = rng.standard_normal((LOOP_B, LOOP_V), dtype=np.float32)
+    x *= np.float32(2.5)
+    return to_bf16_bits(x)
+
+
+def loop_small(step: int = 0) -> Workload:
+    """c4's decode loop at a size the oracle runs every row of: B=64, V=4096
+    bf16 N(0, 2.5) per step, c3's parameter mix, pool [64, 256] written at
+    ``pos0 + step`` with ``pos0 ~ U[1, 128]``."""
+    rng = np.random.default_rng(2104)
+    T, k, p = _c3_params(rng, LOOP_B)
+    prng = np.random.default_rng(3104)
+    pool = prng.integers(0, LOOP_V, LOOP_POOL).astype(np.int32)
+    pos0 = prng.integers(1, 129, LOOP_B).astype(np.int64)
+    rows = prng.permutation(LOOP_POOL[0])[:LOOP_B].astype(np.int64)
+    return Workload("loop_small", BF16, loop_small_logits(step), T, k, p,
+                    np.arange(100, 100 + LOOP_B, dtype=np.int64), step, pool, rows, pos0 + step,
+                    meta={"pos0": pos0})
+
+
+def mixed_input_batch(seed: int, n_req: int = 64, n_prefill: int = 8, pool_rows: int = 256,
+                      pool_cols: int = 4096):
+    """A step's requests as (table_idx, cached_len, device_len): ``n_prefill``
+    prefill or chunked-prefill spans of 1..2048 tokens among single-token
+    decode requests, in distinct pool rows; the pool holds random ids."""
+    rng = np.random.default_rng(seed)
+    pool = rng.integers(0, 152064, (pool_rows, pool_cols)).astype(np.int32)
+    table_idx = rng.permutation(pool_rows)[:n_req].astype(np.int64)
+    device_len = rng.integers(1, pool_cols + 1, n_req).astype(np.int64)
+    cached_len = device_len - 1
+    pre = rng.permutation(n_req)[:n_prefill]
+    span = rng.integers(1, 2049, n_prefill)
+    cached_len[pre] = np.maximum(device_len[pre] - span, 0)
+    return pool, table_idx, cached_len, device_len
+
 
 def tiny(rng: np.random.Generator, B: int, V: int, dtype: str = F32, scale: float = 2.0,
          greedy_frac: float = 0.25, pool_cols: int = 64) -> Workload:
