@@ -302,8 +302,9 @@ GATHER_BYTES_PER_ENTRY = 8 + 8 + 4 + 4     # row, position read; pool id read; i
 
 def bench_c4_loop(args):
     """The scheduler's overlapped decode loop on the c4 workload: per step
-    gather_tokens (input ids at device_len - 1) -> sample_batch -> write_tokens
-    (pool at device_len, host copy); step s waits for step s-1's ticket after
+    sampler_prepare (host parameters -> one copy) -> gather_tokens (input ids
+    at device_len - 1) -> sample_batch -> write_tokens (pool at device_len,
+    host copy); step s waits for step s-1's ticket after
     enqueuing step s.  Logits of a few distinct steps are resident and used in
     rotation while the step counter advances.  Also times gather_tokens alone
     for the decode batch and for a prefill-sized input tuple."""
@@ -320,10 +321,9 @@ def bench_c4_loop(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     bufs = [torch.from_numpy(wl.c4_logits(i).view(np.int16)).to(dev) for i in range(nbuf)]
-    T = torch.from_numpy(w.temperature).to(dev)
-    k = torch.from_numpy(w.top_k).to(dev)
-    p = torch.from_numpy(w.top_p).to(dev)
-    uid = torch.from_numpy(w.uid).to(dev)
+    # request-level parameters on the host, prepared every step
+    hT, hk, hp, hu = (torch.from_numpy(a) for a in (w.temperature, w.top_k, w.top_p, w.uid))
+    blocks = [torch.empty(20 * B, dtype=torch.uint8, device=dev) for _ in range(2)]
     pool = torch.from_numpy(w.pool.copy()).to(dev)
     rows = torch.from_numpy(w.rows).to(dev)
     pos0 = w.meta["pos0"]
@@ -339,9 +339,9 @@ def bench_c4_loop(args):
     stream = torch.cuda.current_stream()
 
     def step(s):
+        prm = sampler.prepare(B, hT, hk, hp, hu, dev_block=blocks[s % 2], stream=stream)
         sampler.gather(pool, rows, in_pos[s], ids_out=ids, stream=stream)
-        sampler.sample(bufs[s % nbuf], temperature=T, top_k=k, top_p=p, uid=uid, step=s,
-                       tokens_out=tokens, stream=stream)
+        sampler.sample(bufs[s % nbuf], step=s, tokens_out=tokens, stream=stream, **prm)
         return sampler.write(pool, rows, out_pos[s], tokens, host_ring[s % 2], stream)
 
     def loop(first, count):
@@ -382,6 +382,14 @@ def bench_c4_loop(args):
         gbs = n * GATHER_BYTES_PER_ENTRY / (us * 1e-6) / 1e9
         return {"entries": n, "avg_us": us, "achieved_GBs": gbs, "frac": gbs / PEAK_HBM_GBS}
 
+    # host cost of one prepare call (staging, clamps and the enqueued copy)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        sampler.prepare(B, hT, hk, hp, hu, dev_block=blocks[i % 2], stream=stream)
+    prep_us = (time.perf_counter() - t1) * 1e6 / args.steps
+    torch.cuda.synchronize()
+
     # a prefill-sized input tuple: every request of the batch runs 1024
     # positions of its row (spans of neighbouring columns)
     pool_big = pool
@@ -396,7 +404,8 @@ def bench_c4_loop(args):
            f"prefill {g_prefill['entries']} entries {g_prefill['avg_us']:.2f} us "
            f"({g_prefill['achieved_GBs']:.0f} GB/s)")
     out = {
-        "metric": "decode-loop steps: sampled rows/sec at B=512, V=152064 (gather + sample + write)",
+        "metric": "decode-loop steps: sampled rows/sec at B=512, V=152064 "
+                  "(prepare + gather + sample + write)",
         "value": B / (ms_per_step * 1e-3),
         "unit": "rows/s",
         "n_gpus": 1,
@@ -410,9 +419,11 @@ def bench_c4_loop(args):
         "data": "synthetic",
         "config": {"workload": "c4 decode loop: B=512 V=152064 bf16 N(0,2.5) logits, c3 parameter "
                                "mix, token pool [512,4096] from per-request positions U[1,2048]; "
-                               "gather -> sample -> write, step s waits for step s-1's host copy",
+                               "prepare -> gather -> sample -> write, step s waits for step "
+                               "s-1's host copy",
                    "B": B, "V": V, "logits_dtype": "bf16", "input_buffers": nbuf,
                    "parallelism": "single GPU"},
+        "prepare_host_us": prep_us,
         "gather_tokens": {"bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
                           "bytes_per_entry": GATHER_BYTES_PER_ENTRY,
                           "decode": g_decode, "prefill": g_prefill},

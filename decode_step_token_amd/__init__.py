@@ -7,12 +7,13 @@ memory; the next step's input ids are gathered from the same pool.  See ``includ
 ctypes binding.
 """
 from ._binding import (EXPORTS, LIB_PATH, SAMPLER_BF16, SAMPLER_DEBUG_TOPK, SAMPLER_F32, Sampler,
-                       SamplerDebug, SamplerError, gather_tokens, load, sample_batch, sampler_check,
-                       sampler_create, sampler_destroy, sampler_query, sampler_strerror,
-                       sampler_wait, write_tokens)
+                       SamplerArgs, SamplerDebug, SamplerError, gather_tokens, load, sample_batch,
+                       sampler_check, sampler_create, sampler_destroy, sampler_prepare,
+                       sampler_query, sampler_strerror, sampler_wait, write_tokens)
 
 __all__ = [
     "EXPORTS", "LIB_PATH", "SAMPLER_BF16", "SAMPLER_DEBUG_TOPK", "SAMPLER_F32", "Sampler",
-    "SamplerDebug", "SamplerError", "gather_tokens", "load", "sample_batch", "sampler_check", "sampler_create",
-    "sampler_destroy", "sampler_query", "sampler_strerror", "sampler_wait", "write_tokens",
+    "SamplerArgs", "SamplerDebug", "SamplerError", "gather_tokens", "load", "sample_batch",
+    "sampler_check", "sampler_create", "sampler_destroy", "sampler_prepare", "sampler_query",
+    "sampler_strerror", "sampler_wait", "write_tokens",
 ]

@@ -27,9 +27,12 @@ SAMPLER_DEBUG_FORCE_EXACT = 1
 STATUS = {0: "SAMPLER_OK", -1: "SAMPLER_EINVAL", -2: "SAMPLER_ENOMEM", -3: "SAMPLER_EHIP",
           -4: "SAMPLER_ENOTPINNED", -5: "SAMPLER_EDEVICE", -6: "SAMPLER_ETICKET"}
 
-EXPORTS = ("sampler_create", "sampler_destroy", "sample_batch", "write_tokens", "gather_tokens",
-           "sampler_wait", "sampler_query", "sampler_check", "sampler_strerror",
+EXPORTS = ("sampler_create", "sampler_destroy", "sampler_prepare", "sample_batch", "write_tokens",
+           "gather_tokens", "sampler_wait", "sampler_query", "sampler_check", "sampler_strerror",
            "sampler_last_error")
+
+PREP_BYTES_PER_REQUEST = 20     # SAMPLER_PREP_BYTES(B) / B
+PREP_SLOTS = 8
 
 
 class SamplerError(RuntimeError):
@@ -42,6 +45,11 @@ class SamplerDebug(ctypes.Structure):
     _fields_ = [("probs_out", ctypes.c_void_p), ("kept_out", ctypes.c_void_p),
                 ("topk_idx_out", ctypes.c_void_p), ("rand_out", ctypes.c_void_p),
                 ("flags", ctypes.c_uint32)]
+
+
+class SamplerArgs(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_void_p), ("top_k", ctypes.c_void_p),
+                ("top_p", ctypes.c_void_p), ("uid", ctypes.c_void_p), ("B", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -62,6 +70,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sample_batch.argtypes = [P, P, P, I64, I32, P, P, P, P, U64, P, ctypes.POINTER(SamplerDebug)]
     lib.write_tokens.argtypes = [P, P, P, I64, I64, P, P, P, I32, P, ctypes.POINTER(U64)]
     lib.gather_tokens.argtypes = [P, P, P, I64, I64, P, P, I64, P]
+    lib.sampler_prepare.argtypes = [P, P, I32, P, P, P, P, P, I64, ctypes.POINTER(SamplerArgs)]
     lib.sampler_wait.argtypes = [P, U64]
     lib.sampler_query.argtypes = [P, U64]
     lib.sampler_check.argtypes = [P]
@@ -69,8 +78,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sampler_strerror.restype = ctypes.c_char_p
     lib.sampler_last_error.argtypes = [P]
     lib.sampler_last_error.restype = ctypes.c_char_p
-    for name in ("sampler_create", "sampler_destroy", "sample_batch", "write_tokens",
-                 "gather_tokens", "sampler_wait", "sampler_query", "sampler_check"):
+    for name in ("sampler_create", "sampler_destroy", "sampler_prepare", "sample_batch",
+                 "write_tokens", "gather_tokens", "sampler_wait", "sampler_query", "sampler_check"):
         getattr(lib, name).restype = INT
     _lib = lib
     return lib
@@ -205,6 +214,62 @@ def gather_tokens(handle, token_pool: torch.Tensor, rows: torch.Tensor, position
     return ids_out
 
 
+def _host(a, name: str, dtype: torch.dtype, n: int):
+    """A host array (NumPy or CPU tensor) as a contiguous CPU tensor, or None."""
+    if a is None:
+        return None
+    t = a if isinstance(a, torch.Tensor) else torch.from_numpy(__import__("numpy").asarray(a))
+    if t.device.type != "cpu":
+        raise ValueError(f"{name} must be host memory")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    t = t.contiguous()
+    if t.numel() != n:
+        raise ValueError(f"{name}: expected {n} elements, got {t.numel()}")
+    return t
+
+
+def sampler_prepare(handle, B: int, temperature=None, top_k=None, top_p=None, uid=None,
+                    dev_block: Optional[torch.Tensor] = None, device=None, stream=None) -> dict:
+    """Sampler.prepare: host parameter arrays -> device tensors for
+    :func:`sample_batch` (``temperature`` / ``top_k`` / ``top_p`` / ``uid``
+    keyword arguments; None where the pages pass None).  ``dev_block`` is a
+    device uint8 tensor of >= 20 * B bytes (allocated here when omitted); the
+    returned tensors are views of it."""
+    hT = _host(temperature, "temperature", torch.float32, B)
+    hk = _host(top_k, "top_k", torch.int32, B)
+    hp = _host(top_p, "top_p", torch.float32, B)
+    hu = _host(uid, "uid", torch.int64, B)
+    if dev_block is None:
+        dev_block = torch.empty(PREP_BYTES_PER_REQUEST * max(B, 1), dtype=torch.uint8,
+                                device=device if device is not None else "cuda")
+    if dev_block.dtype != torch.uint8 or dev_block.device.type != "cuda" or \
+            not dev_block.is_contiguous():
+        raise ValueError("dev_block must be a contiguous uint8 device tensor")
+    out = SamplerArgs()
+    vp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    code = load().sampler_prepare(handle, _stream(stream), int(B), vp(hT), vp(hk), vp(hp), vp(hu),
+                                  ctypes.c_void_p(dev_block.data_ptr()), dev_block.numel(),
+                                  ctypes.byref(out))
+    _check(code, "sampler_prepare", handle)
+    base = dev_block.data_ptr()
+    views = {"uid": dev_block[0:8 * B].view(torch.int64),
+             "temperature": dev_block[8 * B:12 * B].view(torch.float32),
+             "top_k": dev_block[12 * B:16 * B].view(torch.int32),
+             "top_p": dev_block[16 * B:20 * B].view(torch.float32)}
+    offs = {"uid": 0, "temperature": 8 * B, "top_k": 12 * B, "top_p": 16 * B}
+    res = {}
+    for name in ("temperature", "top_k", "top_p", "uid"):
+        ptr = getattr(out, name)
+        if ptr is None:
+            res[name] = None
+        else:
+            if ptr != base + offs[name]:
+                raise RuntimeError(f"sampler_prepare: unexpected {name} address")
+            res[name] = views[name]
+    return res
+
+
 def sampler_wait(handle, ticket: int) -> None:
     _check(load().sampler_wait(handle, int(ticket)), "sampler_wait", handle)
 
@@ -229,6 +294,11 @@ class Sampler:
         self.vocab_size = vocab_size
         self.dtype = dtype
         self.handle = sampler_create(device, max_batch, vocab_size, dtype, seed)
+
+    def prepare(self, B, temperature=None, top_k=None, top_p=None, uid=None, dev_block=None,
+                stream=None) -> dict:
+        return sampler_prepare(self.handle, B, temperature, top_k, top_p, uid, dev_block,
+                               stream=stream)
 
     def sample(self, logits, **kw) -> torch.Tensor:
         return sample_batch(self.handle, logits, **kw)

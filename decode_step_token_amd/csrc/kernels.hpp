@@ -65,5 +65,7 @@ hipError_t launch_sample_exact(const SampleArgs& args, int dtype, hipStream_t st
 hipError_t launch_sample_stream(const SampleArgs& args, int dtype, hipStream_t stream);
 hipError_t launch_write_tokens(const WriteArgs& args, hipStream_t stream);
 hipError_t launch_gather_tokens(const GatherArgs& args, hipStream_t stream);
+// copies n 4-byte words from mapped pinned host memory (its device address)
+hipError_t launch_upload_words(const uint32_t* src_mapped, uint32_t* dst, int n, hipStream_t stream);
 
 }  // namespace dst

@@ -6,7 +6,8 @@
 // plus forward_batch's non-blocking host copy and completion event ("The
 // scheduler skeleton and the offline interface", section "_forward"; "The
 // engine and the sampler", section "forward_batch"); gather_tokens is
-// _forward's input gather from the same pool.
+// _forward's input gather from the same pool; sampler_prepare is
+// Sampler.prepare (host parameters -> pinned staging -> one copy).
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -20,6 +21,11 @@
 namespace {
 
 constexpr int kRing = 256;
+// Completion events only: what the host reads after a wait (the token copy,
+// the status word) is written by the kernels straight into host memory with
+// system-scope stores, so no cache write-back at system scope is needed when
+// an event completes -- and skipping it saves ~2 us of idle GPU per event.
+constexpr unsigned kEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
 // one thread per gathered entry: a dispatch holds fewer than 2^32 work-items
 constexpr int64_t kMaxGather = INT32_MAX;
 // all-greedy batches with at least this many rows fill the GPU with one
@@ -55,6 +61,11 @@ struct dst_sampler {
     hipEvent_t ring[kRing] = {};
     uint64_t ring_ticket[kRing] = {};
     uint64_t issued = 0;               // tickets are 1, 2, 3, ...
+    char* prep_host = nullptr;         // pinned, mapped: SAMPLER_PREP_SLOTS staging buffers
+    char* prep_mapped = nullptr;       // ... as the device addresses them
+    hipEvent_t prep_ev[SAMPLER_PREP_SLOTS] = {};
+    bool prep_used[SAMPLER_PREP_SLOTS] = {};
+    uint32_t prep_next = 0;
     std::string last_error;
 };
 
@@ -91,10 +102,15 @@ int sampler_destroy(dst_sampler* s) {
     if (!s) return SAMPLER_OK;
     DeviceGuard g(s->device);
     if (s->issued) (void)hipEventSynchronize(s->ring[s->issued % kRing]);
+    for (int i = 0; i < SAMPLER_PREP_SLOTS; ++i)
+        if (s->prep_used[i]) (void)hipEventSynchronize(s->prep_ev[i]);
     for (auto& e : s->ring)
+        if (e) (void)hipEventDestroy(e);
+    for (auto& e : s->prep_ev)
         if (e) (void)hipEventDestroy(e);
     if (s->workspace) (void)hipFree(s->workspace);
     if (s->status_host) (void)hipHostFree(s->status_host);
+    if (s->prep_host) (void)hipHostFree(s->prep_host);
     delete s;
     return SAMPLER_OK;
 }
@@ -138,7 +154,15 @@ int sampler_create(dst_sampler** out, int device, int32_t max_batch, int32_t voc
         e = hipHostGetDevicePointer(reinterpret_cast<void**>(&s->status_dev), s->status_host, 0);
     }
     for (int i = 0; e == hipSuccess && i < kRing; ++i)
-        e = hipEventCreateWithFlags(&s->ring[i], hipEventDisableTiming);
+        e = hipEventCreateWithFlags(&s->ring[i], kEventFlags);
+    if (e == hipSuccess)
+        e = hipHostMalloc(reinterpret_cast<void**>(&s->prep_host),
+                          static_cast<size_t>(SAMPLER_PREP_SLOTS) * SAMPLER_PREP_BYTES(max_batch),
+                          hipHostMallocMapped);
+    if (e == hipSuccess)
+        e = hipHostGetDevicePointer(reinterpret_cast<void**>(&s->prep_mapped), s->prep_host, 0);
+    for (int i = 0; e == hipSuccess && i < SAMPLER_PREP_SLOTS; ++i)
+        e = hipEventCreateWithFlags(&s->prep_ev[i], kEventFlags);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         (void)hipGetLastError();
@@ -256,6 +280,70 @@ int gather_tokens(dst_sampler* s, void* stream, const int32_t* token_pool, int64
     dst::GatherArgs a{token_pool, pool_rows, pool_cols, rows, positions, n, ids_out, s->status_dev};
     const hipError_t e = dst::launch_gather_tokens(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(s, SAMPLER_EHIP, "gather_tokens: launch", e);
+    return SAMPLER_OK;
+}
+
+int sampler_prepare(dst_sampler* s, void* stream, int32_t B, const float* temperature,
+                    const int32_t* top_k, const float* top_p, const int64_t* uid, void* dev_block,
+                    int64_t block_bytes, sampler_args* out) {
+    if (!s) return SAMPLER_EINVAL;
+    if (!out) return fail(s, SAMPLER_EINVAL, "sampler_prepare: null out");
+    *out = sampler_args{nullptr, nullptr, nullptr, nullptr, B};
+    if (B < 0 || B > s->max_batch) return fail(s, SAMPLER_EINVAL, "sampler_prepare: B out of range");
+    // a request is greedy iff its temperature is <= 0 (NaN is not)
+    bool all_greedy = true;
+    for (int32_t b = 0; temperature && b < B && all_greedy; ++b) all_greedy = temperature[b] <= 0.0f;
+    if (all_greedy) return SAMPLER_OK;
+    if (!uid) return fail(s, SAMPLER_EINVAL, "sampler_prepare: uid required unless all greedy");
+    if (!dev_block || (reinterpret_cast<uintptr_t>(dev_block) & 7u) != 0)
+        return fail(s, SAMPLER_EINVAL, "sampler_prepare: dev_block null or not 8-byte aligned");
+    const int64_t bytes = SAMPLER_PREP_BYTES(B);
+    if (block_bytes < bytes) return fail(s, SAMPLER_EINVAL, "sampler_prepare: dev_block too small");
+    DeviceGuard g(s->device);
+    const uint32_t slot = s->prep_next;
+    if (s->prep_used[slot]) {
+        // the copy that last read this staging buffer must have finished
+        const hipError_t we = hipEventSynchronize(s->prep_ev[slot]);
+        if (we != hipSuccess) return fail(s, SAMPLER_EHIP, "sampler_prepare: staging wait", we);
+    }
+    char* h = s->prep_host + static_cast<size_t>(slot) * SAMPLER_PREP_BYTES(s->max_batch);
+    int64_t* h_uid = reinterpret_cast<int64_t*>(h);
+    float* h_t = reinterpret_cast<float*>(h + 8 * static_cast<size_t>(B));
+    int32_t* h_k = reinterpret_cast<int32_t*>(h + 12 * static_cast<size_t>(B));
+    float* h_p = reinterpret_cast<float*>(h + 16 * static_cast<size_t>(B));
+    // the pages' values, in double as Python computes them, stored as fp32;
+    // max(a, b) and min(a, b) keep their first argument unless the second is
+    // strictly larger (smaller), as Python's do
+    const double kMin = 1e-6;
+    bool any_k = false, any_p = false;
+    for (int32_t b = 0; b < B; ++b) {
+        const double t = temperature[b] <= 0.0f ? 0.0 : static_cast<double>(temperature[b]);
+        h_t[b] = static_cast<float>(kMin > t ? kMin : t);
+        const int32_t k = top_k ? top_k[b] : -1;
+        h_k[b] = k >= 1 ? k : s->vocab;
+        any_k = any_k || h_k[b] != s->vocab;
+        const double p0 = top_p ? static_cast<double>(top_p[b]) : 1.0;
+        const double p1 = kMin > p0 ? kMin : p0;
+        const double p2 = 1.0 < p1 ? 1.0 : p1;
+        h_p[b] = static_cast<float>(p2);
+        any_p = any_p || p2 < 1.0;
+        h_uid[b] = uid[b];
+    }
+    // the upload is a kernel reading the staging buffer through its mapping
+    const char* hm = s->prep_mapped + static_cast<size_t>(slot) * SAMPLER_PREP_BYTES(s->max_batch);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = dst::launch_upload_words(reinterpret_cast<const uint32_t*>(hm),
+                                            static_cast<uint32_t*>(dev_block),
+                                            static_cast<int>(bytes / 4), st);
+    if (e == hipSuccess) e = hipEventRecord(s->prep_ev[slot], st);
+    if (e != hipSuccess) return fail(s, SAMPLER_EHIP, "sampler_prepare: copy", e);
+    s->prep_used[slot] = true;
+    s->prep_next = (slot + 1) % SAMPLER_PREP_SLOTS;
+    char* d = static_cast<char*>(dev_block);
+    out->uid = reinterpret_cast<const int64_t*>(d);
+    out->temperature = reinterpret_cast<const float*>(d + 8 * static_cast<size_t>(B));
+    out->top_k = any_k ? reinterpret_cast<const int32_t*>(d + 12 * static_cast<size_t>(B)) : nullptr;
+    out->top_p = any_p ? reinterpret_cast<const float*>(d + 16 * static_cast<size_t>(B)) : nullptr;
     return SAMPLER_OK;
 }
 

@@ -8,7 +8,8 @@
 // CPU never needs the token values.
 //
 // One thread per request; an out-of-range (row, col) skips the write and
-// raises the handle's status word (mapped pinned host memory, plain store).
+// raises the handle's status word (mapped pinned host memory, system-scope
+// store).
 // The host copy of forward_batch is the same kernel: each thread also stores
 // its token into the caller's pinned buffer through its device mapping, with
 // system scope, so the completion event covers it.
@@ -40,7 +41,7 @@ __global__ __launch_bounds__(kWriteBlock) void write_tokens_kernel(WriteArgs a) 
     if (r >= 0 && r < a.pool_rows && c >= 0 && c < a.pool_cols) {
         a.pool[r * a.pool_cols + c] = tok;
     } else {
-        *reinterpret_cast<volatile uint32_t*>(a.status) = 1u;
+        __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     if (a.host) __hip_atomic_store(a.host + b, tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(kGatherBlock) void gather_tokens_kernel(GatherArgs 
     if (r >= 0 && r < a.pool_rows && c >= 0 && c < a.pool_cols) {
         id = a.pool[r * a.pool_cols + c];
     } else {
-        *reinterpret_cast<volatile uint32_t*>(a.status) = 1u;
+        __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     a.ids_out[i] = id;
 }

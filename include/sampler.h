@@ -25,11 +25,12 @@
  *   - "dev" pointers are device memory of the handle's device (e.g. from
  *     hipMalloc or torch); "host" pointers are host memory.  The caller owns
  *     every buffer it passes in; the library owns only the handle, a device
- *     workspace allocated once in sampler_create, a small pinned status word
- *     and a ring of completion events.
+ *     workspace allocated once in sampler_create, a small pinned status word,
+ *     pinned staging buffers for sampler_prepare and rings of events.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     sample_batch, write_tokens and gather_tokens only enqueue work on
- *     `stream`: they never allocate and never wait for the device.
+ *     `stream`: they never allocate and never wait for the device
+ *     (sampler_prepare may wait for its own staging copies, see there).
  *   - Argument errors that the host can see are reported synchronously and
  *     nothing is enqueued.  Parameter *values* in device memory are never
  *     errors: they are clamped on the device as Sampler.prepare clamps them.
@@ -105,8 +106,10 @@ typedef struct sampler_debug {
  *   vocab_size  V, the row length of every logits tensor (1 .. 1<<30).
  *   logits_dtype SAMPLER_F32 or SAMPLER_BF16 (raw bf16 bit patterns).
  *   seed        key of the counter-based generator (the engine seeds with 42).
- * Allocates the device workspace (hipMalloc) and events; the only call that
- * allocates.  Errors: SAMPLER_EINVAL, SAMPLER_ENOMEM, SAMPLER_EHIP.
+ * Allocates the device workspace (hipMalloc), the pinned staging buffers
+ * (hipHostMalloc, SAMPLER_PREP_SLOTS x 20 x max_batch bytes) and events; the
+ * only call that allocates.  Errors: SAMPLER_EINVAL, SAMPLER_ENOMEM,
+ * SAMPLER_EHIP.
  */
 DST_API int sampler_create(dst_sampler** out, int device, int32_t max_batch, int32_t vocab_size,
                    int32_t logits_dtype, uint64_t seed);
@@ -193,6 +196,54 @@ DST_API int write_tokens(dst_sampler* s, void* stream, int32_t* token_pool, int6
 DST_API int gather_tokens(dst_sampler* s, void* stream, const int32_t* token_pool,
                           int64_t pool_rows, int64_t pool_cols, const int64_t* rows,
                           const int64_t* positions, int64_t n, int32_t* ids_out);
+
+/*
+ * sampler_prepare -- Sampler.prepare moved into the library ("The engine and
+ * the sampler", section "The sampler"): the batch's request-level sampling
+ * parameters, given as host arrays, become the per-request device tensors
+ * that sample_batch reads, through one pinned staging buffer and one
+ * asynchronous upload on `stream` (a small kernel that reads the staging
+ * buffer through its device mapping).
+ *   B           requests, 0 .. max_batch.
+ *   temperature host [B] fp32, or NULL (every request greedy).  A request is
+ *               greedy iff its temperature is <= 0.  If every request is
+ *               greedy nothing is copied and out->temperature is NULL
+ *               (sample_batch then takes the plain argmax path).
+ *   top_k       host [B] int32, or NULL (no request sets it).
+ *   top_p       host [B] fp32, or NULL (no request sets it).
+ *   uid         host [B] int64; required unless every request is greedy.
+ *   dev_block   dev, caller-owned, 8-byte aligned, at least
+ *               SAMPLER_PREP_BYTES(B) bytes; receives, packed:
+ *               uid int64[B] | temperature fp32[B] | top_k int32[B] | top_p fp32[B]
+ *               with the pages' values: temperature max(0 if greedy else T,
+ *               1e-6); top_k k if k >= 1 else vocab_size; top_p
+ *               min(max(p, 1e-6), 1) (each computed in double, stored
+ *               rounded to fp32).  The caller must not reuse it before the
+ *               sample_batch that reads it has run (stream order suffices).
+ *   out         host: device pointers into dev_block for sample_batch, each
+ *               NULL where the pages pass None: temperature (all greedy),
+ *               top_k (every entry equals vocab_size), top_p (no entry
+ *               below 1); uid NULL with temperature.
+ * The host arrays are read before the call returns (pageable memory is
+ * fine).  The library keeps SAMPLER_PREP_SLOTS pinned staging buffers in
+ * rotation; a call waits on the host only if the upload issued from the same
+ * buffer that many calls earlier has not finished.
+ * Errors: SAMPLER_EINVAL (synchronous, nothing enqueued); SAMPLER_EHIP.
+ */
+#define SAMPLER_PREP_BYTES(B) ((int64_t)(B) * 20)
+#define SAMPLER_PREP_SLOTS 8
+
+typedef struct sampler_args {
+    const float*   temperature;
+    const int32_t* top_k;
+    const float*   top_p;
+    const int64_t* uid;
+    int32_t        B;
+} sampler_args;
+
+DST_API int sampler_prepare(dst_sampler* s, void* stream, int32_t B, const float* temperature,
+                            const int32_t* top_k, const float* top_p, const int64_t* uid,
+                            void* dev_block, int64_t block_bytes, sampler_args* out);
 
 /*
  * sampler_wait -- block until the ticket's work (and its host copy) is done:

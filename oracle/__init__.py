@@ -16,15 +16,17 @@ Pins (each in ``tests/test_oracle_pins.py``):
 * ``write_tokens``: NumPy fancy-index assignment.
 * ``gather_tokens`` / ``input_tuple``: NumPy fancy indexing, a write-then-gather
   round trip, and the packed positions of a hand-worked prefill + decode batch.
+* ``prepare``: hand-worked batches (clamps and the None rules), and that the
+  per-row routing of the prepared tensors equals that of the raw parameters.
 """
 from .philox import philox4x64, request_uniform, request_word, uniform24
 from .sampler_ref import (CUT_BAND, DRAW_BAND, MIN_P, MIN_T, RowParams, RowResult,
                           descending_order, filter_sorted, gather_tokens, input_tuple,
-                          inverse_cdf, row_params, sample_batch, sample_row, widen_logits,
+                          inverse_cdf, prepare, row_params, sample_batch, sample_row, widen_logits,
                           write_tokens)
 
 __all__ = [
     "philox4x64", "request_uniform", "request_word", "uniform24", "CUT_BAND", "DRAW_BAND",
     "MIN_P", "MIN_T", "RowParams", "RowResult", "descending_order", "filter_sorted",
-    "gather_tokens", "input_tuple", "inverse_cdf", "row_params", "sample_batch", "sample_row", "widen_logits", "write_tokens",
+    "gather_tokens", "input_tuple", "inverse_cdf", "prepare", "row_params", "sample_batch", "sample_row", "widen_logits", "write_tokens",
 ]

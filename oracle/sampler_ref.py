@@ -272,3 +272,31 @@ def input_tuple(table_idx, cached_len, device_len):
             rows.append(int(r))
             pos.append(c)
     return np.asarray(rows, dtype=np.int64), np.asarray(pos, dtype=np.int64)
+
+
+def prepare(V: int, temperature, top_k, top_p):
+    """``Sampler.prepare`` for a batch ("The engine and the sampler", section
+    "The sampler"), from request-level parameters (each array may be None:
+    not set by any request).  A request is greedy iff its temperature is
+    <= 0.  The values are computed on Python floats as the pages do, then
+    stored as float32 / int32.
+
+    Returns (temperature, top_k, top_p): float32 / int32 / float32 arrays, or
+    None where the pages pass None."""
+    B = 0
+    for a in (temperature, top_k, top_p):
+        if a is not None:
+            B = len(a)
+    T = [0.0] * B if temperature is None else [float(np.float32(t)) for t in temperature]
+    greedy = [not (t > 0.0) if t == t else False for t in T]       # NaN is not greedy
+    if all(greedy):
+        return None, None, None
+    min_t = min_p = 1e-6
+    ts = [max(0.0 if g else t, min_t) for g, t in zip(greedy, T)]
+    ks_in = [-1] * B if top_k is None else [int(k) for k in top_k]
+    ks = [k if k >= 1 else V for k in ks_in]
+    ps_in = [1.0] * B if top_p is None else [float(np.float32(p)) for p in top_p]
+    ps = [min(max(p, min_p), 1.0) for p in ps_in]
+    out_k = np.array(ks, dtype=np.int32) if any(k != V for k in ks) else None
+    out_p = np.array(ps, dtype=np.float32) if any(p < 1.0 for p in ps) else None
+    return np.array(ts, dtype=np.float32), out_k, out_p

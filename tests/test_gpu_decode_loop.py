@@ -4,7 +4,9 @@ The scheduler's step ("The scheduler skeleton and the offline interface",
 sections "Preparing a batch" and "_forward") gathers the input ids from the
 token pool at (row, position), runs the model, samples, and writes the
 tokens back at (row, device_len); its overlap loop waits for step N-1's host
-copy only after step N is enqueued.  The gather is compared bit for bit with
+copy only after step N is enqueued; the sampling parameters are prepared from
+host arrays every step ("The engine and the sampler", section "The
+sampler").  The gather is compared bit for bit with
 the oracle's ``token_pool[rows, positions]``; the loops compare every step's
 gathered ids, tokens, host copies and the final pool.
 """
@@ -124,15 +126,18 @@ def test_gather_sees_write_on_same_stream():
 
 
 def _overlap_loop(s, w0, logits_dev, steps, debug):
-    """Enqueue gather -> sample -> write for every step; wait for step N-1's
-    ticket only after step N is enqueued, reading its pinned ring slot."""
+    """Enqueue prepare -> gather -> sample -> write for every step; wait for
+    step N-1's ticket only after step N is enqueued, reading its pinned ring
+    slot."""
     B = w0.B
     pool = _dev(w0.pool.copy())
     rows = _dev(w0.rows)
     pos0 = w0.meta["pos0"]
     in_pos = [_dev(pos0 + st - 1) for st in range(steps)]
     out_pos = [_dev(pos0 + st) for st in range(steps)]
-    T, k, p, uid = _dev(w0.temperature), _dev(w0.top_k), _dev(w0.top_p), _dev(w0.uid)
+    # the parameters are prepared every step from host arrays, as the
+    # scheduler does; two device blocks alternate
+    blocks = [torch.empty(20 * B, dtype=torch.uint8, device="cuda") for _ in range(2)]
     ring = [torch.full((B,), -7, dtype=torch.int32).pin_memory() for _ in range(2)]
     ids = [torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(steps)]
     toks = [torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(steps)]
@@ -142,9 +147,10 @@ def _overlap_loop(s, w0, logits_dev, steps, debug):
     host = []
     prev = None
     for st in range(steps):
+        args = s.prepare(B, w0.temperature, w0.top_k, w0.top_p, w0.uid,
+                         dev_block=blocks[st % 2])
         s.gather(pool, rows, in_pos[st], ids_out=ids[st])
-        s.sample(logits_dev[st], temperature=T, top_k=k, top_p=p, uid=uid, step=st,
-                 tokens_out=toks[st], debug=dbg[st])
+        s.sample(logits_dev[st], step=st, tokens_out=toks[st], debug=dbg[st], **args)
         t = s.write(pool, rows, out_pos[st], toks[st], ring[st % 2])
         if prev is not None:
             s.wait(prev)

@@ -18,7 +18,7 @@ import scipy.stats
 import oracle
 from oracle import (filter_sorted, inverse_cdf, philox4x64, request_uniform, request_word,
                     row_params, sample_batch, sample_row, widen_logits, write_tokens)
-from oracle import gather_tokens, input_tuple
+from oracle import gather_tokens, input_tuple, prepare
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 M64 = (1 << 64) - 1
@@ -406,6 +406,57 @@ def test_gather_equals_concatenated_request_slices():
     got, bad = gather_tokens(pool, rows, pos)
     want = np.concatenate([ids[lo:hi] for _, lo, hi, ids in reqs])
     assert np.array_equal(got, want) and not bad
+
+
+# ------------------------------------------------------------ prepare ---
+
+def test_prepare_hand_worked_batch():
+    """Greedy requests get the tiny temperature, top-k below 1 becomes V,
+    top-p is clamped into [1e-6, 1] ("The engine and the sampler", section
+    "The sampler")."""
+    V = 100
+    T = np.array([0.0, 0.7, -1.0, 1.3, 2e-7], dtype=np.float32)
+    k = np.array([-1, 50, 0, 1, 103], dtype=np.int32)
+    p = np.array([0.9, 1.0, 1.5, 1e-9, 0.25], dtype=np.float32)
+    ts, ks, ps = prepare(V, T, k, p)
+    assert ts.dtype == np.float32 and ks.dtype == np.int32 and ps.dtype == np.float32
+    assert ts.tolist() == [np.float32(1e-6), np.float32(0.7), np.float32(1e-6), np.float32(1.3),
+                           np.float32(1e-6)]
+    assert ks.tolist() == [100, 50, 100, 1, 103]
+    assert ps.tolist() == [np.float32(0.9), 1.0, 1.0, np.float32(1e-6), 0.25]
+
+
+def test_prepare_none_rules():
+    V = 64
+    # every request greedy: no tensors at all (the plain argmax path)
+    assert prepare(V, np.array([0.0, -2.0], np.float32), np.array([5, 7], np.int32),
+                   np.array([0.5, 0.5], np.float32)) == (None, None, None)
+    assert prepare(V, None, np.array([5], np.int32), None) == (None, None, None)
+    T = np.array([0.0, 0.8], np.float32)
+    # top-k set by nobody (every entry ends up V), top-p never below 1
+    ts, ks, ps = prepare(V, T, np.array([-1, V], np.int32), np.array([1.0, 3.0], np.float32))
+    assert ts is not None and ks is None and ps is None
+    ts, ks, ps = prepare(V, T, None, None)
+    assert ks is None and ps is None
+    # one request is enough to build each tensor
+    _, ks, ps = prepare(V, T, np.array([-1, V + 1], np.int32), np.array([1.0, 0.99999], np.float32))
+    assert ks.tolist() == [V, V + 1] and ps is not None and ps[1] < 1.0
+
+
+def test_prepare_keeps_every_rows_routing():
+    """sample_batch clamps the prepared tensors again; for every request the
+    effective (greedy, T, k, p) equals that of its raw parameters."""
+    rng = np.random.default_rng(12)
+    V, B = 500, 400
+    T = rng.choice(np.array([0.0, -1.0, 1e-9, 5e-7, 1e-6, 2e-6, 0.3, 0.7, 1.5], np.float32), B)
+    k = rng.choice(np.array([-7, -1, 0, 1, 2, 50, V - 1, V, V + 9], np.int32), B)
+    p = rng.choice(np.array([1e-12, 1e-6, 0.2, 0.9, 1.0, 1.7], np.float32), B)
+    ts, ks, ps = prepare(V, T, k, p)
+    for b in range(B):
+        raw = row_params(V, float(max(T[b], 0.0)), int(k[b]), float(p[b]))
+        prep = row_params(V, float(ts[b]), None if ks is None else int(ks[b]),
+                          None if ps is None else float(ps[b]))
+        assert raw == prep, (b, T[b], k[b], p[b])
 
 
 def test_module_header_marks_test_infrastructure():

@@ -104,6 +104,22 @@ def _gather_wraps_negative(pool, rows, positions):
     return ids, bool((~ok).any())
 
 
+_real_prepare = sr.prepare
+
+
+def _prepare_k_strict(V, temperature, top_k, top_p):
+    # "k > 1" for "k >= 1": a top-k of 1 would be dropped
+    k2 = None if top_k is None else np.where(np.asarray(top_k) == 1, -1, top_k).astype(np.int32)
+    return _real_prepare(V, temperature, k2, top_p)
+
+
+def _prepare_p_tensor_always(V, temperature, top_k, top_p):
+    ts, ks, ps = _real_prepare(V, temperature, top_k, top_p)
+    if ts is not None and ps is None:
+        ps = np.ones(len(ts), dtype=np.float32)
+    return ts, ks, ps
+
+
 def _input_tuple_inclusive(table_idx, cached_len, device_len):
     # off by one: runs [cached_len, device_len]
     return _real_input_tuple(table_idx, cached_len, [int(d) + 1 for d in device_len])
@@ -136,6 +152,8 @@ PLANTS = [
     ("gather_tokens", _gather_wraps_negative,
      ["test_gather_tokens_out_of_range_is_reported_not_wrapped"]),
     ("input_tuple", _input_tuple_inclusive, ["test_input_tuple_hand_worked_batch"]),
+    ("prepare", _prepare_k_strict, ["test_prepare_hand_worked_batch"]),
+    ("prepare", _prepare_p_tensor_always, ["test_prepare_none_rules"]),
 ]
 
 
@@ -143,7 +161,7 @@ PLANTS = [
 def test_planted_sampler_mistake_is_caught(monkeypatch, attr, bad, pin_names):
     monkeypatch.setattr(sr, attr, bad)
     for mod_name in ("filter_sorted", "inverse_cdf", "write_tokens", "gather_tokens",
-                     "input_tuple"):
+                     "input_tuple", "prepare"):
         if attr == mod_name:
             monkeypatch.setattr(pins, mod_name, bad)
     with pytest.raises(Exception):    # a failed assertion, or the oracle breaking outright
