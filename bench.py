@@ -298,16 +298,19 @@ def main():
 
 
 GATHER_BYTES_PER_ENTRY = 8 + 8 + 4 + 4     # row, position read; pool id read; id written
+PAGE_BYTES_PER_POSITION = 4 + 4            # page start read (page size 1), table cell written
 
 
 def bench_c4_loop(args):
     """The scheduler's overlapped decode loop on the c4 workload: per step
-    sampler_prepare (host parameters -> one copy) -> gather_tokens (input ids
+    sampler_prepare (host parameters -> one upload) -> write_page_table (the
+    step's new KV page per request, page size 1) -> gather_tokens (input ids
     at device_len - 1) -> sample_batch -> write_tokens (pool at device_len,
-    host copy); step s waits for step s-1's ticket after
-    enqueuing step s.  Logits of a few distinct steps are resident and used in
-    rotation while the step counter advances.  Also times gather_tokens alone
-    for the decode batch and for a prefill-sized input tuple."""
+    host copy); step s waits for step s-1's ticket after enqueuing step s.
+    Logits of a few distinct steps are resident and used in rotation while
+    the step counter advances.  Also times gather_tokens and
+    write_page_table alone, for the decode batch and for prefill-sized
+    inputs."""
     import numpy as np
     import torch
 
@@ -332,6 +335,14 @@ def bench_c4_loop(args):
         raise SystemExit(f"bench.py: {total} steps run past the pool's {w.pool.shape[1]} columns")
     in_pos = [torch.from_numpy(pos0 + s - 1).to(dev) for s in range(total)]
     out_pos = [torch.from_numpy(pos0 + s).to(dev) for s in range(total)]
+    # page table of the same shape as the pool, page size 1: each step gives
+    # every request the page for position device_len - 1, taken from the
+    # front of a device free list
+    page_table = torch.full(tuple(w.pool.shape), -1, dtype=torch.int32, device=dev)
+    free_list = torch.arange(B * w.pool.shape[1], dtype=torch.int32, device=dev)
+    req_rows = w.rows.astype(np.int64)
+    cached = [pos0 + s - 1 for s in range(total)]
+    devlen = [pos0 + s for s in range(total)]
     ids = torch.empty(B, dtype=torch.int32, device=dev)
     tokens = torch.empty(B, dtype=torch.int32, device=dev)
     host_ring = [torch.empty(B, dtype=torch.int32).pin_memory() for _ in range(2)]
@@ -340,6 +351,9 @@ def bench_c4_loop(args):
 
     def step(s):
         prm = sampler.prepare(B, hT, hk, hp, hu, dev_block=blocks[s % 2], stream=stream)
+        off = (s * B) % (free_list.numel() - B)
+        sampler.write_page_table(page_table, req_rows, cached[s], devlen[s],
+                                 free_list[off:off + B], 1, stream)
         sampler.gather(pool, rows, in_pos[s], ids_out=ids, stream=stream)
         sampler.sample(bufs[s % nbuf], step=s, tokens_out=tokens, stream=stream, **prm)
         return sampler.write(pool, rows, out_pos[s], tokens, host_ring[s % 2], stream)
@@ -363,26 +377,27 @@ def bench_c4_loop(args):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    def time_gather(r, c, reps):
-        out = torch.empty(r.numel(), dtype=torch.int32, device=dev)
-        for _ in range(3):
-            sampler.gather(pool_big, r, c, ids_out=out, stream=stream)
+    def queued(launch, reps):
+        """Mean time of `reps` launches run back to back: the stream is held
+        in a spin kernel while they are enqueued."""
+        for _ in range(2):
+            launch()
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
-        # hold the stream in a spin kernel while the launches are enqueued, so
-        # that they run back to back rather than at the host's launch rate
-        torch.cuda._sleep(int(reps * 20e3))
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(max(reps, 16) * 40e3))
         ev0.record(stream)
         for _ in range(reps):
-            sampler.gather(pool_big, r, c, ids_out=out, stream=stream)
+            launch()
         ev1.record(stream)
         torch.cuda.synchronize()
-        us = ev0.elapsed_time(ev1) * 1e3 / reps
-        n = r.numel()
-        gbs = n * GATHER_BYTES_PER_ENTRY / (us * 1e-6) / 1e9
+        return ev0.elapsed_time(ev1) * 1e3 / reps
+
+    def rate(n, nbytes, us):
+        gbs = nbytes / (us * 1e-6) / 1e9
         return {"entries": n, "avg_us": us, "achieved_GBs": gbs, "frac": gbs / PEAK_HBM_GBS}
 
-    # host cost of one prepare call (staging, clamps and the enqueued copy)
+    # host cost of one prepare call (staging, clamps and the enqueued upload)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for i in range(args.steps):
@@ -390,22 +405,36 @@ def bench_c4_loop(args):
     prep_us = (time.perf_counter() - t1) * 1e6 / args.steps
     torch.cuda.synchronize()
 
-    # a prefill-sized input tuple: every request of the batch runs 1024
-    # positions of its row (spans of neighbouring columns)
-    pool_big = pool
+    # prefill-sized inputs: every request of the batch runs 1024 positions of
+    # its row (spans of neighbouring columns)
     span = 1024
     pr = torch.arange(B, device=dev, dtype=torch.int64).repeat_interleave(span)
     pc = torch.arange(span, device=dev, dtype=torch.int64).repeat(B)
-    g_decode = time_gather(rows, in_pos[0], args.steps)
-    g_prefill = time_gather(pr, pc, args.steps)
+    out_ids = torch.empty(B * span, dtype=torch.int32, device=dev)
+    g_decode = rate(B, B * GATHER_BYTES_PER_ENTRY,
+                    queued(lambda: sampler.gather(pool, rows, in_pos[0], ids_out=ids, stream=stream),
+                           args.steps))
+    g_prefill = rate(B * span, B * span * GATHER_BYTES_PER_ENTRY,
+                     queued(lambda: sampler.gather(pool, pr, pc, ids_out=out_ids, stream=stream),
+                            args.steps))
+    # the page-table write keeps its host records in 8 staging buffers that a
+    # later call reuses only after the kernel ran, so at most 8 are queued
+    zeros = np.zeros(B, dtype=np.int64)
+    p_decode = rate(B, B * PAGE_BYTES_PER_POSITION,
+                    queued(lambda: sampler.write_page_table(page_table, req_rows, cached[0],
+                                                            devlen[0], free_list[:B], 1, stream), 8))
+    p_prefill = rate(B * span, B * span * PAGE_BYTES_PER_POSITION,
+                     queued(lambda: sampler.write_page_table(page_table, req_rows, zeros,
+                                                             zeros + span, free_list[:B * span], 1,
+                                                             stream), 8))
     sampler.check()
     sampler.close()
     eprint(f"bench: {ms_per_step * 1e3:.1f} us/loop step; gather decode {g_decode['avg_us']:.2f} us, "
-           f"prefill {g_prefill['entries']} entries {g_prefill['avg_us']:.2f} us "
-           f"({g_prefill['achieved_GBs']:.0f} GB/s)")
+           f"prefill {g_prefill['avg_us']:.2f} us; page table decode {p_decode['avg_us']:.2f} us, "
+           f"prefill {p_prefill['avg_us']:.2f} us")
     out = {
         "metric": "decode-loop steps: sampled rows/sec at B=512, V=152064 "
-                  "(prepare + gather + sample + write)",
+                  "(prepare + page table + gather + sample + write)",
         "value": B / (ms_per_step * 1e-3),
         "unit": "rows/s",
         "n_gpus": 1,
@@ -418,15 +447,18 @@ def bench_c4_loop(args):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "c4 decode loop: B=512 V=152064 bf16 N(0,2.5) logits, c3 parameter "
-                               "mix, token pool [512,4096] from per-request positions U[1,2048]; "
-                               "prepare -> gather -> sample -> write, step s waits for step "
-                               "s-1's host copy",
+                               "mix, token pool and page table [512,4096], per-request positions "
+                               "from U[1,2048], page size 1; prepare -> page table -> gather -> "
+                               "sample -> write, step s waits for step s-1's host copy",
                    "B": B, "V": V, "logits_dtype": "bf16", "input_buffers": nbuf,
                    "parallelism": "single GPU"},
         "prepare_host_us": prep_us,
         "gather_tokens": {"bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
                           "bytes_per_entry": GATHER_BYTES_PER_ENTRY,
                           "decode": g_decode, "prefill": g_prefill},
+        "write_page_table": {"bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                             "bytes_per_position": PAGE_BYTES_PER_POSITION,
+                             "decode": p_decode, "prefill": p_prefill},
     }
     print(json.dumps(out), flush=True)
 

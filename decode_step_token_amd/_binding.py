@@ -28,8 +28,8 @@ STATUS = {0: "SAMPLER_OK", -1: "SAMPLER_EINVAL", -2: "SAMPLER_ENOMEM", -3: "SAMP
           -4: "SAMPLER_ENOTPINNED", -5: "SAMPLER_EDEVICE", -6: "SAMPLER_ETICKET"}
 
 EXPORTS = ("sampler_create", "sampler_destroy", "sampler_prepare", "sample_batch", "write_tokens",
-           "gather_tokens", "sampler_wait", "sampler_query", "sampler_check", "sampler_strerror",
-           "sampler_last_error")
+           "gather_tokens", "write_page_table", "sampler_wait", "sampler_query", "sampler_check",
+           "sampler_strerror", "sampler_last_error")
 
 PREP_BYTES_PER_REQUEST = 20     # SAMPLER_PREP_BYTES(B) / B
 PREP_SLOTS = 8
@@ -70,6 +70,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sample_batch.argtypes = [P, P, P, I64, I32, P, P, P, P, U64, P, ctypes.POINTER(SamplerDebug)]
     lib.write_tokens.argtypes = [P, P, P, I64, I64, P, P, P, I32, P, ctypes.POINTER(U64)]
     lib.gather_tokens.argtypes = [P, P, P, I64, I64, P, P, I64, P]
+    lib.write_page_table.argtypes = [P, P, P, I64, I64, P, P, P, I32, P, I64, I32]
     lib.sampler_prepare.argtypes = [P, P, I32, P, P, P, P, P, I64, ctypes.POINTER(SamplerArgs)]
     lib.sampler_wait.argtypes = [P, U64]
     lib.sampler_query.argtypes = [P, U64]
@@ -79,7 +80,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sampler_last_error.argtypes = [P]
     lib.sampler_last_error.restype = ctypes.c_char_p
     for name in ("sampler_create", "sampler_destroy", "sampler_prepare", "sample_batch",
-                 "write_tokens", "gather_tokens", "sampler_wait", "sampler_query", "sampler_check"):
+                 "write_tokens", "gather_tokens", "write_page_table", "sampler_wait",
+                 "sampler_query", "sampler_check"):
         getattr(lib, name).restype = INT
     _lib = lib
     return lib
@@ -270,6 +272,28 @@ def sampler_prepare(handle, B: int, temperature=None, top_k=None, top_p=None, ui
     return res
 
 
+def write_page_table(handle, page_table: torch.Tensor, table_idx, cached_len, device_len,
+                     page_starts: Optional[torch.Tensor], page_size: int, stream=None) -> None:
+    """Write the pages newly needed by each request into its page-table row
+    (``table_idx`` / ``cached_len`` / ``device_len``: host int64 arrays;
+    ``page_starts``: device int32, one entry per new page, request order)."""
+    if page_table.dim() != 2 or not page_table.is_contiguous():
+        raise ValueError("page_table must be a contiguous [R, C] tensor")
+    dev = page_table.device
+    n = len(table_idx)
+    ht = _host(table_idx, "table_idx", torch.int64, n)
+    hc = _host(cached_len, "cached_len", torch.int64, n)
+    hd = _host(device_len, "device_len", torch.int64, n)
+    n_pages = 0 if page_starts is None else page_starts.numel()
+    vp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    code = load().write_page_table(
+        handle, _stream(stream), _ptr(page_table, "page_table", torch.int32, None, dev),
+        page_table.shape[0], page_table.shape[1], vp(ht), vp(hc), vp(hd), n,
+        None if n_pages == 0 else _ptr(page_starts, "page_starts", torch.int32, n_pages, dev),
+        n_pages, int(page_size))
+    _check(code, "write_page_table", handle)
+
+
 def sampler_wait(handle, ticket: int) -> None:
     _check(load().sampler_wait(handle, int(ticket)), "sampler_wait", handle)
 
@@ -308,6 +332,11 @@ class Sampler:
 
     def gather(self, token_pool, rows, positions, ids_out=None, stream=None) -> torch.Tensor:
         return gather_tokens(self.handle, token_pool, rows, positions, ids_out, stream)
+
+    def write_page_table(self, page_table, table_idx, cached_len, device_len, page_starts,
+                         page_size, stream=None) -> None:
+        write_page_table(self.handle, page_table, table_idx, cached_len, device_len, page_starts,
+                         page_size, stream)
 
     def wait(self, ticket: int) -> None:
         sampler_wait(self.handle, ticket)

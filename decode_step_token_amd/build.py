@@ -20,7 +20,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdst_sampler.so")
 
 SOURCES = ["argmax.hip", "sample_exact.hip", "sample_stream.hip", "write_tokens.hip",
-           "prepare.hip", "sampler_api.hip"]
+           "prepare.hip", "page_table.hip", "sampler_api.hip"]
 HEADERS = ["device_common.hpp", "kernels.hpp", "exact_path.hpp"]
 
 ARCH = "gfx950"

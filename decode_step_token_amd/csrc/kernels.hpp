@@ -59,12 +59,22 @@ struct GatherArgs {
     uint32_t* status;          // mapped pinned host word; set to 1 on a bad (row, position)
 };
 
+struct PageTableArgs {
+    int32_t* table;
+    int64_t rows, cols;
+    const int64_t* records;    // device address of mapped pinned records: row, first, npos, page base
+    const int32_t* page_starts;
+    int64_t page_size;
+    uint32_t* status;          // mapped pinned host word; set to 1 on a bad (row, column)
+};
+
 hipError_t launch_argmax(const ArgmaxArgs& args, int dtype, hipStream_t stream);
 void argmax_plan(int B, int V, int dtype, int* chunks, int* chunk_len);
 hipError_t launch_sample_exact(const SampleArgs& args, int dtype, hipStream_t stream);
 hipError_t launch_sample_stream(const SampleArgs& args, int dtype, hipStream_t stream);
 hipError_t launch_write_tokens(const WriteArgs& args, hipStream_t stream);
 hipError_t launch_gather_tokens(const GatherArgs& args, hipStream_t stream);
+hipError_t launch_write_page_table(const PageTableArgs& args, int n_records, hipStream_t stream);
 // copies n 4-byte words from mapped pinned host memory (its device address)
 hipError_t launch_upload_words(const uint32_t* src_mapped, uint32_t* dst, int n, hipStream_t stream);
 

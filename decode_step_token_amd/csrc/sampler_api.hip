@@ -7,7 +7,8 @@
 // scheduler skeleton and the offline interface", section "_forward"; "The
 // engine and the sampler", section "forward_batch"); gather_tokens is
 // _forward's input gather from the same pool; sampler_prepare is
-// Sampler.prepare (host parameters -> pinned staging -> one copy).
+// Sampler.prepare (host parameters -> pinned staging -> one copy);
+// write_page_table is the cache manager's paged allocation write.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -26,6 +27,8 @@ constexpr int kRing = 256;
 // system-scope stores, so no cache write-back at system scope is needed when
 // an event completes -- and skipping it saves ~2 us of idle GPU per event.
 constexpr unsigned kEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
+// page-table staging: (row, first position, positions, first page) per request
+constexpr size_t kPageRecordBytes = 4 * sizeof(int64_t);
 // one thread per gathered entry: a dispatch holds fewer than 2^32 work-items
 constexpr int64_t kMaxGather = INT32_MAX;
 // all-greedy batches with at least this many rows fill the GPU with one
@@ -66,6 +69,11 @@ struct dst_sampler {
     hipEvent_t prep_ev[SAMPLER_PREP_SLOTS] = {};
     bool prep_used[SAMPLER_PREP_SLOTS] = {};
     uint32_t prep_next = 0;
+    int64_t* pt_host = nullptr;        // pinned, mapped: page-table record staging
+    int64_t* pt_mapped = nullptr;
+    hipEvent_t pt_ev[SAMPLER_PREP_SLOTS] = {};
+    bool pt_used[SAMPLER_PREP_SLOTS] = {};
+    uint32_t pt_next = 0;
     std::string last_error;
 };
 
@@ -102,15 +110,20 @@ int sampler_destroy(dst_sampler* s) {
     if (!s) return SAMPLER_OK;
     DeviceGuard g(s->device);
     if (s->issued) (void)hipEventSynchronize(s->ring[s->issued % kRing]);
-    for (int i = 0; i < SAMPLER_PREP_SLOTS; ++i)
+    for (int i = 0; i < SAMPLER_PREP_SLOTS; ++i) {
         if (s->prep_used[i]) (void)hipEventSynchronize(s->prep_ev[i]);
+        if (s->pt_used[i]) (void)hipEventSynchronize(s->pt_ev[i]);
+    }
     for (auto& e : s->ring)
         if (e) (void)hipEventDestroy(e);
     for (auto& e : s->prep_ev)
         if (e) (void)hipEventDestroy(e);
+    for (auto& e : s->pt_ev)
+        if (e) (void)hipEventDestroy(e);
     if (s->workspace) (void)hipFree(s->workspace);
     if (s->status_host) (void)hipHostFree(s->status_host);
     if (s->prep_host) (void)hipHostFree(s->prep_host);
+    if (s->pt_host) (void)hipHostFree(s->pt_host);
     delete s;
     return SAMPLER_OK;
 }
@@ -163,6 +176,14 @@ int sampler_create(dst_sampler** out, int device, int32_t max_batch, int32_t voc
         e = hipHostGetDevicePointer(reinterpret_cast<void**>(&s->prep_mapped), s->prep_host, 0);
     for (int i = 0; e == hipSuccess && i < SAMPLER_PREP_SLOTS; ++i)
         e = hipEventCreateWithFlags(&s->prep_ev[i], kEventFlags);
+    if (e == hipSuccess)
+        e = hipHostMalloc(reinterpret_cast<void**>(&s->pt_host),
+                          static_cast<size_t>(SAMPLER_PREP_SLOTS) * kPageRecordBytes * max_batch,
+                          hipHostMallocMapped);
+    if (e == hipSuccess)
+        e = hipHostGetDevicePointer(reinterpret_cast<void**>(&s->pt_mapped), s->pt_host, 0);
+    for (int i = 0; e == hipSuccess && i < SAMPLER_PREP_SLOTS; ++i)
+        e = hipEventCreateWithFlags(&s->pt_ev[i], kEventFlags);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         (void)hipGetLastError();
@@ -344,6 +365,58 @@ int sampler_prepare(dst_sampler* s, void* stream, int32_t B, const float* temper
     out->temperature = reinterpret_cast<const float*>(d + 8 * static_cast<size_t>(B));
     out->top_k = any_k ? reinterpret_cast<const int32_t*>(d + 12 * static_cast<size_t>(B)) : nullptr;
     out->top_p = any_p ? reinterpret_cast<const float*>(d + 16 * static_cast<size_t>(B)) : nullptr;
+    return SAMPLER_OK;
+}
+
+int write_page_table(dst_sampler* s, void* stream, int32_t* page_table, int64_t table_rows,
+                     int64_t table_cols, const int64_t* table_idx, const int64_t* cached_len,
+                     const int64_t* device_len, int32_t n_req, const int32_t* page_starts,
+                     int64_t n_pages, int32_t page_size) {
+    if (!s) return SAMPLER_EINVAL;
+    if (n_req < 0 || n_req > s->max_batch) return fail(s, SAMPLER_EINVAL, "write_page_table: n_req out of range");
+    if (page_size < 1) return fail(s, SAMPLER_EINVAL, "write_page_table: page_size < 1");
+    if (!page_table || table_rows < 1 || table_cols < 1 || table_cols > INT32_MAX)
+        return fail(s, SAMPLER_EINVAL, "write_page_table: null, empty or too wide page table");
+    if (n_req > 0 && (!table_idx || !cached_len || !device_len))
+        return fail(s, SAMPLER_EINVAL, "write_page_table: null request arrays");
+    if (n_pages < 0 || (n_pages > 0 && !page_starts))
+        return fail(s, SAMPLER_EINVAL, "write_page_table: bad page_starts / n_pages");
+    DeviceGuard g(s->device);
+    const uint32_t slot = s->pt_next;
+    if (s->pt_used[slot]) {
+        const hipError_t we = hipEventSynchronize(s->pt_ev[slot]);
+        if (we != hipSuccess) return fail(s, SAMPLER_EHIP, "write_page_table: staging wait", we);
+    }
+    const size_t slot_words = 4 * static_cast<size_t>(s->max_batch);
+    int64_t* rec = s->pt_host + slot * slot_words;
+    const int64_t ps = page_size;
+    int64_t pages = 0;
+    int n_rec = 0;
+    for (int32_t r = 0; r < n_req; ++r) {
+        const int64_t c = cached_len[r], d = device_len[r];
+        if (c < 0 || d < 0) return fail(s, SAMPLER_EINVAL, "write_page_table: negative length");
+        const int64_t first = c / ps + (c % ps != 0);     // ceil(c / ps)
+        const int64_t last = d / ps + (d % ps != 0);
+        if (last <= first) continue;
+        if (table_idx[r] < 0 || table_idx[r] >= table_rows || last > table_cols / ps)
+            return fail(s, SAMPLER_EINVAL, "write_page_table: page range outside the table");
+        rec[4 * n_rec + 0] = table_idx[r];
+        rec[4 * n_rec + 1] = first * ps;
+        rec[4 * n_rec + 2] = (last - first) * ps;
+        rec[4 * n_rec + 3] = pages;
+        pages += last - first;
+        ++n_rec;
+    }
+    if (pages != n_pages) return fail(s, SAMPLER_EINVAL, "write_page_table: n_pages differs from the pages needed");
+    if (n_rec == 0) return SAMPLER_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    dst::PageTableArgs a{page_table, table_rows, table_cols, s->pt_mapped + slot * slot_words,
+                         page_starts, ps, s->status_dev};
+    hipError_t e = dst::launch_write_page_table(a, n_rec, st);
+    if (e == hipSuccess) e = hipEventRecord(s->pt_ev[slot], st);
+    if (e != hipSuccess) return fail(s, SAMPLER_EHIP, "write_page_table: launch", e);
+    s->pt_used[slot] = true;
+    s->pt_next = (slot + 1) % SAMPLER_PREP_SLOTS;
     return SAMPLER_OK;
 }
 

@@ -16,7 +16,9 @@
  *   "The scheduler skeleton and the offline interface", sections "Preparing a
  *       batch" (_make_write_tuple) and "_forward" -- token_pool[row, col] =
  *       token, a column of -1 lands in the last column; the step's input ids
- *       are gathered from the same pool at (row, position).
+ *       are gathered from the same pool at (row, position);
+ *   "CacheManager: allocation, release and admission control" -- the page
+ *       table rows of a step's newly allocated KV pages.
  *
  * Conventions for every entry point:
  *   - Return value: 0 (SAMPLER_OK) or a negative SAMPLER_E* code.  No C++
@@ -30,7 +32,8 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     sample_batch, write_tokens and gather_tokens only enqueue work on
  *     `stream`: they never allocate and never wait for the device
- *     (sampler_prepare may wait for its own staging copies, see there).
+ *     (sampler_prepare and write_page_table may wait for their own staging
+ *     buffers, see there).
  *   - Argument errors that the host can see are reported synchronously and
  *     nothing is enqueued.  Parameter *values* in device memory are never
  *     errors: they are clamped on the device as Sampler.prepare clamps them.
@@ -107,9 +110,9 @@ typedef struct sampler_debug {
  *   logits_dtype SAMPLER_F32 or SAMPLER_BF16 (raw bf16 bit patterns).
  *   seed        key of the counter-based generator (the engine seeds with 42).
  * Allocates the device workspace (hipMalloc), the pinned staging buffers
- * (hipHostMalloc, SAMPLER_PREP_SLOTS x 20 x max_batch bytes) and events; the
- * only call that allocates.  Errors: SAMPLER_EINVAL, SAMPLER_ENOMEM,
- * SAMPLER_EHIP.
+ * (hipHostMalloc, SAMPLER_PREP_SLOTS x (20 + 32) x max_batch bytes) and
+ * events; the only call that allocates.  Errors: SAMPLER_EINVAL,
+ * SAMPLER_ENOMEM, SAMPLER_EHIP.
  */
 DST_API int sampler_create(dst_sampler** out, int device, int32_t max_batch, int32_t vocab_size,
                    int32_t logits_dtype, uint64_t seed);
@@ -196,6 +199,35 @@ DST_API int write_tokens(dst_sampler* s, void* stream, int32_t* token_pool, int6
 DST_API int gather_tokens(dst_sampler* s, void* stream, const int32_t* token_pool,
                           int64_t pool_rows, int64_t pool_cols, const int64_t* rows,
                           const int64_t* positions, int64_t n, int32_t* ids_out);
+
+/*
+ * write_page_table -- the cache manager's paged allocation write ("CacheManager:
+ * allocation, release and admission control", sections "The free-page list"
+ * and "Allocating pages for this step's tokens"): request r's new pages are
+ * [ceil(cached_len[r] / page_size), ceil(device_len[r] / page_size)); going
+ * through the requests in order, each new page takes the next entry of
+ * page_starts, and every position p of the page gets
+ * page_table[table_idx[r], p] = page_start + p % page_size.
+ *   page_table  dev [table_rows, table_cols] int32, row-major.
+ *   table_idx, cached_len, device_len  host [n_req] int64 (read before the
+ *               call returns); 0 <= n_req <= max_batch; lengths >= 0.
+ *   page_starts dev [n_pages] int32: the first token location of each newly
+ *               allocated page, in request order (for example the front of
+ *               a device free list).
+ *   n_pages     the number of new pages; must equal the sum over requests of
+ *               max(0, ceil(device_len / page_size) - ceil(cached_len /
+ *               page_size)).
+ *   page_size   >= 1.
+ * The host stages one record per request with new pages in pinned memory
+ * (SAMPLER_PREP_SLOTS buffers in rotation, as sampler_prepare) and one
+ * kernel on `stream` expands them.  n_pages == 0 enqueues nothing.
+ * Errors (synchronous, nothing enqueued): SAMPLER_EINVAL for bad arguments,
+ * n_pages not matching, or a page range outside the table; SAMPLER_EHIP.
+ */
+DST_API int write_page_table(dst_sampler* s, void* stream, int32_t* page_table,
+                             int64_t table_rows, int64_t table_cols, const int64_t* table_idx,
+                             const int64_t* cached_len, const int64_t* device_len, int32_t n_req,
+                             const int32_t* page_starts, int64_t n_pages, int32_t page_size);
 
 /*
  * sampler_prepare -- Sampler.prepare moved into the library ("The engine and

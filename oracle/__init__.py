@@ -18,15 +18,23 @@ Pins (each in ``tests/test_oracle_pins.py``):
   round trip, and the packed positions of a hand-worked prefill + decode batch.
 * ``prepare``: hand-worked batches (clamps and the None rules), and that the
   per-row routing of the prepared tensors equals that of the raw parameters.
+* ``PagePool`` / ``paged_info`` / ``page_to_token`` / ``write_page_table``:
+  the pages' page-aligned allocation test (row [0..7], free pages 6, 6, 5, a
+  new page starting at a multiple of 4), their worked page count (page size
+  4, cached 6, device 9: one page), and brute force over random batches
+  (every position holds its own page's location plus its offset, no location
+  twice).
 """
 from .philox import philox4x64, request_uniform, request_word, uniform24
 from .sampler_ref import (CUT_BAND, DRAW_BAND, MIN_P, MIN_T, RowParams, RowResult,
                           descending_order, filter_sorted, gather_tokens, input_tuple,
-                          inverse_cdf, prepare, row_params, sample_batch, sample_row, widen_logits,
-                          write_tokens)
+                          inverse_cdf, PagePool, page_to_token, paged_info, prepare,
+                          row_params, sample_batch, sample_row, widen_logits,
+                          write_page_table, write_tokens)
 
 __all__ = [
     "philox4x64", "request_uniform", "request_word", "uniform24", "CUT_BAND", "DRAW_BAND",
     "MIN_P", "MIN_T", "RowParams", "RowResult", "descending_order", "filter_sorted",
-    "gather_tokens", "input_tuple", "inverse_cdf", "prepare", "row_params", "sample_batch", "sample_row", "widen_logits", "write_tokens",
+    "gather_tokens", "input_tuple", "inverse_cdf", "PagePool", "page_to_token", "paged_info",
+    "prepare", "write_page_table", "row_params", "sample_batch", "sample_row", "widen_logits", "write_tokens",
 ]

@@ -300,3 +300,85 @@ def prepare(V: int, temperature, top_k, top_p):
     out_k = np.array(ks, dtype=np.int32) if any(k != V for k in ks) else None
     out_p = np.array(ps, dtype=np.float32) if any(p < 1.0 for p in ps) else None
     return np.array(ts, dtype=np.float32), out_k, out_p
+
+
+def _div_ceil(a: int, b: int) -> int:
+    return -(-int(a) // int(b))
+
+
+def page_to_token(page_starts, page_size: int) -> np.ndarray:
+    """Token locations of allocated pages: each page's first location plus
+    every offset inside the page ("CacheManager: allocation, release and
+    admission control", section "The free-page list": free slots hold the
+    first token location of each page).  The pages do not print
+    ``_page_to_token``; this is the plainest reading of that section."""
+    starts = np.asarray(page_starts, dtype=np.int64)
+    return (starts[:, None] + np.arange(page_size, dtype=np.int64)[None, :]).reshape(-1)
+
+
+def write_page_table(page_table: np.ndarray, allocated: np.ndarray, info, page_size: int):
+    """``_write_page_table`` (same page, section "Allocating pages for this
+    step's tokens"): (row, column) pairs built on the host request by request
+    over [first_page * page_size, last_page * page_size), then one indexed
+    assignment of the allocated token locations.  An out-of-range
+    pair is skipped and reported.
+
+    Returns (new page table, out_of_range flag)."""
+    rows, cols = [], []
+    for table_idx, first_page, last_page in info:
+        lo, hi = first_page * page_size, last_page * page_size
+        rows.extend([int(table_idx)] * (hi - lo))
+        cols.extend(range(lo, hi))
+    assert len(rows) == len(allocated), "allocated locations must match the positions"
+    out = page_table.copy()
+    R, C = out.shape
+    bad = False
+    for r, c, v in zip(rows, cols, allocated):
+        if 0 <= r < R and 0 <= c < C:
+            out[r, c] = np.int32(v)
+        else:
+            bad = True
+    return out, bad
+
+
+def paged_info(table_idx, cached_len, device_len, page_size: int):
+    """``allocate_paged``'s per-request page ranges (same page and section):
+    pages [ceil(cached_len /
+    page_size), ceil(device_len / page_size)) are new; requests without a new
+    page are left out.  Returns (info list, number of new pages)."""
+    info, needed = [], 0
+    for t, c, d in zip(table_idx, cached_len, device_len):
+        first, last = _div_ceil(c, page_size), _div_ceil(d, page_size)
+        if last > first:
+            needed += last - first
+            info.append((int(t), first, last))
+    return info, needed
+
+
+class PagePool:
+    """The free-page list of the cache manager with the naive cache (no
+    eviction; same page, sections "The free-page list" and "_allocate"): free
+    slots start as every page's first token location, and allocation takes
+    pages from the front."""
+
+    def __init__(self, num_pages: int, page_size: int):
+        self.page_size = page_size
+        self.free_slots = np.arange(num_pages, dtype=np.int64) * page_size
+
+    def allocate(self, needed_pages: int) -> np.ndarray:
+        assert needed_pages <= len(self.free_slots), "not enough free pages"
+        out = self.free_slots[:needed_pages].copy()
+        self.free_slots = self.free_slots[needed_pages:]
+        return out
+
+    def allocate_paged(self, page_table: np.ndarray, table_idx, cached_len, device_len):
+        """Allocate this step's pages and write them into the page table.
+        Returns (new page table, page starts allocated)."""
+        info, needed = paged_info(table_idx, cached_len, device_len, self.page_size)
+        if needed == 0:
+            return page_table.copy(), np.zeros(0, dtype=np.int64)
+        starts = self.allocate(needed)
+        out, bad = write_page_table(page_table, page_to_token(starts, self.page_size), info,
+                                    self.page_size)
+        assert not bad
+        return out, starts

@@ -18,7 +18,8 @@ import scipy.stats
 import oracle
 from oracle import (filter_sorted, inverse_cdf, philox4x64, request_uniform, request_word,
                     row_params, sample_batch, sample_row, widen_logits, write_tokens)
-from oracle import gather_tokens, input_tuple, prepare
+from oracle import (PagePool, gather_tokens, input_tuple, page_to_token, paged_info, prepare,
+                    write_page_table)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 M64 = (1 << 64) - 1
@@ -457,6 +458,64 @@ def test_prepare_keeps_every_rows_routing():
         prep = row_params(V, float(ts[b]), None if ks is None else int(ks[b]),
                           None if ps is None else float(ps[b]))
         assert raw == prep, (b, T[b], k[b], p[b])
+
+
+# --------------------------------------------------------- page table ---
+
+def test_page_aligned_allocation_pages_test():
+    """The pages' test of page-aligned allocation ("CacheManager: allocation,
+    release and admission control", section "Tests"): 8 pages of 4 tokens; a
+    6-token prompt in table row 2 takes 2 pages (row [0..7], 6 pages free);
+    device_len 7 needs none; device_len 9 takes a third page whose location
+    is a multiple of 4 (5 free)."""
+    pool = PagePool(num_pages=8, page_size=4)
+    table = np.full((4, 32), -1, dtype=np.int32)
+    table, _ = pool.allocate_paged(table, [2], [0], [6])
+    assert table[2, :8].tolist() == [0, 1, 2, 3, 4, 5, 6, 7] and len(pool.free_slots) == 6
+    table, _ = pool.allocate_paged(table, [2], [6], [7])
+    assert len(pool.free_slots) == 6
+    table, _ = pool.allocate_paged(table, [2], [8], [9])
+    assert len(pool.free_slots) == 5 and table[2, 8] % 4 == 0
+    assert table[2, 8:12].tolist() == [8, 9, 10, 11]
+
+
+def test_paged_info_worked_count():
+    """Page size 4, cached_len 6, device_len 9: pages 0-1 exist, 3 are needed,
+    one is allocated (same page, section "Allocating pages for this step's
+    tokens")."""
+    info, needed = paged_info([5], [6], [9], 4)
+    assert needed == 1 and info == [(5, 2, 3)]
+    info, needed = paged_info([0, 1, 2], [0, 3, 7], [1, 4, 7], 1)
+    assert needed == 2 and info == [(0, 0, 1), (1, 3, 4)]
+
+
+def test_page_table_brute_force():
+    """Every written position holds its own page's first location plus its
+    offset, no location is written twice, and nothing else changes."""
+    rng = np.random.default_rng(13)
+    for ps in (1, 2, 4, 16):
+        R, C = 24, 256
+        table0 = rng.integers(-50, -1, (R, C)).astype(np.int32)
+        n = 12
+        tidx = rng.permutation(R)[:n]
+        dev = rng.integers(0, C + 1, n)
+        cached = np.minimum(dev, rng.integers(0, C + 1, n))
+        info, needed = paged_info(tidx, cached, dev, ps)
+        starts = rng.permutation(4 * needed + 8)[:needed] * ps
+        table, bad = write_page_table(table0, page_to_token(starts, ps), info, ps)
+        assert not bad
+        seen = set()
+        k = 0
+        touched = np.zeros_like(table0, dtype=bool)
+        for t, first, last in info:
+            for page in range(first, last):
+                for o in range(ps):
+                    v = int(table[t, page * ps + o])
+                    assert v == starts[k] + o and v not in seen
+                    seen.add(v)
+                    touched[t, page * ps + o] = True
+                k += 1
+        assert k == needed and np.array_equal(table[~touched], table0[~touched])
 
 
 def test_module_header_marks_test_infrastructure():

@@ -120,6 +120,26 @@ def _prepare_p_tensor_always(V, temperature, top_k, top_p):
     return ts, ks, ps
 
 
+_real_paged_info = sr.paged_info
+_real_page_to_token = sr.page_to_token
+
+
+def _paged_info_floor(table_idx, cached_len, device_len, page_size):
+    # floor instead of ceil for the first page: a partly filled page again
+    info, needed = [], 0
+    for t, c, d in zip(table_idx, cached_len, device_len):
+        first, last = int(c) // page_size, -(-int(d) // page_size)
+        if last > first:
+            needed += last - first
+            info.append((int(t), first, last))
+    return info, needed
+
+
+def _page_to_token_scaled(page_starts, page_size):
+    # treats the free slots as page numbers
+    return _real_page_to_token(np.asarray(page_starts) * page_size, page_size)
+
+
 def _input_tuple_inclusive(table_idx, cached_len, device_len):
     # off by one: runs [cached_len, device_len]
     return _real_input_tuple(table_idx, cached_len, [int(d) + 1 for d in device_len])
@@ -154,6 +174,8 @@ PLANTS = [
     ("input_tuple", _input_tuple_inclusive, ["test_input_tuple_hand_worked_batch"]),
     ("prepare", _prepare_k_strict, ["test_prepare_hand_worked_batch"]),
     ("prepare", _prepare_p_tensor_always, ["test_prepare_none_rules"]),
+    ("paged_info", _paged_info_floor, ["test_paged_info_worked_count"]),
+    ("page_to_token", _page_to_token_scaled, ["test_page_aligned_allocation_pages_test"]),
 ]
 
 
@@ -161,7 +183,7 @@ PLANTS = [
 def test_planted_sampler_mistake_is_caught(monkeypatch, attr, bad, pin_names):
     monkeypatch.setattr(sr, attr, bad)
     for mod_name in ("filter_sorted", "inverse_cdf", "write_tokens", "gather_tokens",
-                     "input_tuple", "prepare"):
+                     "input_tuple", "prepare", "paged_info", "page_to_token"):
         if attr == mod_name:
             monkeypatch.setattr(pins, mod_name, bad)
     with pytest.raises(Exception):    # a failed assertion, or the oracle breaking outright

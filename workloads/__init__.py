@@ -286,3 +286,20 @@ def tiny(rng: np.random.Generator, B: int, V: int, dtype: str = F32, scale: floa
     uid = rng.integers(-(1 << 40), 1 << 40, B).astype(np.int64)
     return Workload(f"tiny_{B}x{V}_{dtype}", dtype, logits, T, k.astype(np.int32),
                     p.astype(np.float32), uid, int(rng.integers(0, 1 << 20)), pool, rows, cols)
+
+
+def paged_batch(seed: int, n_req: int = 300, table_rows: int = 512, table_cols: int = 4096,
+                page_size: int = 1, prefill_frac: float = 0.25):
+    """One step's requests for the page-table write: distinct table rows,
+    prefill spans (cached_len 0 or a chunk boundary, device_len up to the
+    table width) and decode requests (one new token); a free list of page
+    starts (multiples of page_size, shuffled) large enough for the step."""
+    rng = np.random.default_rng(seed)
+    table_idx = rng.permutation(table_rows)[:n_req].astype(np.int64)
+    device_len = rng.integers(1, table_cols + 1, n_req).astype(np.int64)
+    cached_len = device_len - 1
+    pre = rng.random(n_req) < prefill_frac
+    cached_len[pre] = np.maximum(device_len[pre] - rng.integers(1, 2049, int(pre.sum())), 0)
+    num_pages = (table_rows * table_cols) // page_size
+    free_slots = rng.permutation(num_pages).astype(np.int64) * page_size
+    return table_idx, cached_len, device_len, free_slots
