@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 METRIC = "sampled rows/sec and achieved HBM GB/s (% of peak) at B=256, V=151936"
 PARAM_BYTES_PER_ROW = 4 + 4 + 4 + 8 + 4   # T, top_k, top_p, uid read; token written
+C3_MIN_P_VALUES = [0.0, 0.02, 0.05, 0.1]
 WRITE_BYTES_PER_ROW = 8 + 8 + 4 + 4       # row, col, token read; pool cell written
 # calibration copy for the HBM byte counters: torch's elementwise negation of
 # one fp32 logits buffer into another (one read and one write of each byte)
@@ -136,7 +137,7 @@ def cpu_baseline(w, seconds: float):
     n = 0
     for b in range(w.B):
         oracle.sample_batch(w.logits, w.dtype, w.temperature, w.top_k, w.top_p, w.uid, w.step,
-                            w.seed, rows=[b])
+                            w.seed, rows=[b], min_p=w.min_p)
         n += 1
         if time.perf_counter() - t0 > seconds:
             break
@@ -159,10 +160,10 @@ def main():
                     help="record counter-measured bytes per launch in profiles/traffic.json")
     ap.add_argument("--traffic-command", default="",
                     help="with --write-traffic: the profiling command, stored with the figures")
-    ap.add_argument("--workload", choices=("c3", "c4loop"), default="c3",
-                    help="c3: the headline sampler step (default); c4loop: the overlapped "
-                         "decode loop gather -> sample -> write at B=512 V=152064 bf16, plus "
-                         "the input gather alone")
+    ap.add_argument("--workload", choices=("c3", "c3minp", "c4loop"), default="c3",
+                    help="c3: the headline sampler step (default); c3minp: the same batch with "
+                         "a per-request min_p; c4loop: the overlapped decode loop (prepare, page "
+                         "table, gather, sample, write) at B=512 V=152064 bf16")
     args = ap.parse_args()
 
     if args.write_traffic:
@@ -187,6 +188,10 @@ def main():
 
     eprint("bench: generating the B=256 V=151936 fp32 workload")
     w = wl.c3()
+    minp = None
+    if args.workload == "c3minp":
+        w = wl.with_min_p(w, C3_MIN_P_VALUES, 8)
+        minp = torch.from_numpy(w.min_p).to("cuda:0")
     B, V = w.B, w.V
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -206,7 +211,7 @@ def main():
 
     def step(s):
         sampler.sample(bufs[s % len(bufs)], temperature=T, top_k=k, top_p=p, uid=uid, step=s,
-                       tokens_out=tokens, stream=stream)
+                       tokens_out=tokens, stream=stream, min_p=minp)
         return sampler.write(pool, rows, cols0, tokens, host_ring[s % 2], stream)
 
     eprint(f"bench: warmup {args.warmup} steps")
@@ -242,7 +247,8 @@ def main():
     ev0.record(stream)
     for i in range(args.steps):
         sampler.sample(bufs[i % len(bufs)], temperature=T, top_k=k, top_p=p, uid=uid,
-                       step=args.warmup + args.steps + i, tokens_out=tokens, stream=stream)
+                       step=args.warmup + args.steps + i, tokens_out=tokens, stream=stream,
+                       min_p=minp)
     ev1.record(stream)
     torch.cuda.synchronize()
     kernel_ms_total = ev0.elapsed_time(ev1)
@@ -264,7 +270,7 @@ def main():
     eprint(f"bench: {ms_per_step * 1e3:.1f} us/step, sample_batch kernel avg "
            f"{avg_kernel_ms * 1e3:.1f} us, {achieved:.0f} GB/s")
 
-    traffic = load_traffic("sample_batch", "c3")
+    traffic = load_traffic("sample_batch", "c3") if minp is None else None
     cpu = None
     if not args.no_cpu_baseline:
         eprint(f"bench: timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
@@ -285,7 +291,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "c3: B=256 V=151936 fp32 2*Gumbel+rank-4 logits, per-request "
                                "T~U[0.3,1.5], top_k in {1,20,50,off}, top_p in {1,0.95,0.8}; "
-                               "token pool [256,4096]",
+                               "token pool [256,4096]"
+                               + ("; min_p in {0,0.02,0.05,0.1}" if minp is not None else ""),
                    "B": B, "V": V, "logits_dtype": "f32", "input_buffers": len(bufs),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -326,7 +333,8 @@ def bench_c4_loop(args):
     bufs = [torch.from_numpy(wl.c4_logits(i).view(np.int16)).to(dev) for i in range(nbuf)]
     # request-level parameters on the host, prepared every step
     hT, hk, hp, hu = (torch.from_numpy(a) for a in (w.temperature, w.top_k, w.top_p, w.uid))
-    blocks = [torch.empty(20 * B, dtype=torch.uint8, device=dev) for _ in range(2)]
+    blocks = [torch.empty(dst._binding.PREP_BYTES_PER_REQUEST * B, dtype=torch.uint8, device=dev)
+              for _ in range(2)]
     pool = torch.from_numpy(w.pool.copy()).to(dev)
     rows = torch.from_numpy(w.rows).to(dev)
     pos0 = w.meta["pos0"]

@@ -31,7 +31,7 @@ EXPORTS = ("sampler_create", "sampler_destroy", "sampler_prepare", "sample_batch
            "gather_tokens", "write_page_table", "sampler_wait", "sampler_query", "sampler_check",
            "sampler_strerror", "sampler_last_error")
 
-PREP_BYTES_PER_REQUEST = 20     # SAMPLER_PREP_BYTES(B) / B
+PREP_BYTES_PER_REQUEST = 24     # SAMPLER_PREP_BYTES(B) / B
 PREP_SLOTS = 8
 
 
@@ -49,7 +49,8 @@ class SamplerDebug(ctypes.Structure):
 
 class SamplerArgs(ctypes.Structure):
     _fields_ = [("temperature", ctypes.c_void_p), ("top_k", ctypes.c_void_p),
-                ("top_p", ctypes.c_void_p), ("uid", ctypes.c_void_p), ("B", ctypes.c_int32)]
+                ("top_p", ctypes.c_void_p), ("min_p", ctypes.c_void_p), ("uid", ctypes.c_void_p),
+                ("B", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -67,11 +68,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                              ctypes.c_int)
     lib.sampler_create.argtypes = [ctypes.POINTER(P), INT, I32, I32, I32, U64]
     lib.sampler_destroy.argtypes = [P]
-    lib.sample_batch.argtypes = [P, P, P, I64, I32, P, P, P, P, U64, P, ctypes.POINTER(SamplerDebug)]
+    lib.sample_batch.argtypes = [P, P, P, I64, I32, P, P, P, P, P, U64, P,
+                                 ctypes.POINTER(SamplerDebug)]
     lib.write_tokens.argtypes = [P, P, P, I64, I64, P, P, P, I32, P, ctypes.POINTER(U64)]
     lib.gather_tokens.argtypes = [P, P, P, I64, I64, P, P, I64, P]
     lib.write_page_table.argtypes = [P, P, P, I64, I64, P, P, P, I32, P, I64, I32]
-    lib.sampler_prepare.argtypes = [P, P, I32, P, P, P, P, P, I64, ctypes.POINTER(SamplerArgs)]
+    lib.sampler_prepare.argtypes = [P, P, I32, P, P, P, P, P, P, I64, ctypes.POINTER(SamplerArgs)]
     lib.sampler_wait.argtypes = [P, U64]
     lib.sampler_query.argtypes = [P, U64]
     lib.sampler_check.argtypes = [P]
@@ -139,7 +141,7 @@ def sampler_destroy(handle) -> None:
 def sample_batch(handle, logits: torch.Tensor, temperature=None, top_k=None, top_p=None,
                  uid=None, step: int = 0, tokens_out: Optional[torch.Tensor] = None,
                  stream=None, debug: Optional[dict] = None, row_stride: Optional[int] = None,
-                 B: Optional[int] = None) -> torch.Tensor:
+                 B: Optional[int] = None, min_p=None) -> torch.Tensor:
     """``logits``: [B, >=V] float32 or bf16 tensor (bf16 may also be passed as
     int16/uint16 bit patterns); returns (or fills) ``tokens_out`` int32 [B]."""
     if logits.dim() != 2:
@@ -164,6 +166,7 @@ def sample_batch(handle, logits: torch.Tensor, temperature=None, top_k=None, top
         _ptr(temperature, "temperature", torch.float32, B, dev),
         _ptr(top_k, "top_k", torch.int32, B, dev),
         _ptr(top_p, "top_p", torch.float32, B, dev),
+        _ptr(min_p, "min_p", torch.float32, B, dev),
         _ptr(uid, "uid", torch.int64, B, dev),
         int(step) & ((1 << 64) - 1),
         _ptr(tokens_out, "tokens_out", torch.int32, None, dev),
@@ -232,15 +235,17 @@ def _host(a, name: str, dtype: torch.dtype, n: int):
 
 
 def sampler_prepare(handle, B: int, temperature=None, top_k=None, top_p=None, uid=None,
-                    dev_block: Optional[torch.Tensor] = None, device=None, stream=None) -> dict:
+                    dev_block: Optional[torch.Tensor] = None, device=None, stream=None,
+                    min_p=None) -> dict:
     """Sampler.prepare: host parameter arrays -> device tensors for
-    :func:`sample_batch` (``temperature`` / ``top_k`` / ``top_p`` / ``uid``
-    keyword arguments; None where the pages pass None).  ``dev_block`` is a
-    device uint8 tensor of >= 20 * B bytes (allocated here when omitted); the
-    returned tensors are views of it."""
+    :func:`sample_batch` (``temperature`` / ``top_k`` / ``top_p`` / ``min_p``
+    / ``uid`` keyword arguments; None where the pages pass None).
+    ``dev_block`` is a device uint8 tensor of >= 24 * B bytes (allocated here
+    when omitted); the returned tensors are views of it."""
     hT = _host(temperature, "temperature", torch.float32, B)
     hk = _host(top_k, "top_k", torch.int32, B)
     hp = _host(top_p, "top_p", torch.float32, B)
+    hm = _host(min_p, "min_p", torch.float32, B)
     hu = _host(uid, "uid", torch.int64, B)
     if dev_block is None:
         dev_block = torch.empty(PREP_BYTES_PER_REQUEST * max(B, 1), dtype=torch.uint8,
@@ -250,18 +255,19 @@ def sampler_prepare(handle, B: int, temperature=None, top_k=None, top_p=None, ui
         raise ValueError("dev_block must be a contiguous uint8 device tensor")
     out = SamplerArgs()
     vp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
-    code = load().sampler_prepare(handle, _stream(stream), int(B), vp(hT), vp(hk), vp(hp), vp(hu),
-                                  ctypes.c_void_p(dev_block.data_ptr()), dev_block.numel(),
-                                  ctypes.byref(out))
+    code = load().sampler_prepare(handle, _stream(stream), int(B), vp(hT), vp(hk), vp(hp), vp(hm),
+                                  vp(hu), ctypes.c_void_p(dev_block.data_ptr()),
+                                  dev_block.numel(), ctypes.byref(out))
     _check(code, "sampler_prepare", handle)
     base = dev_block.data_ptr()
     views = {"uid": dev_block[0:8 * B].view(torch.int64),
              "temperature": dev_block[8 * B:12 * B].view(torch.float32),
              "top_k": dev_block[12 * B:16 * B].view(torch.int32),
-             "top_p": dev_block[16 * B:20 * B].view(torch.float32)}
-    offs = {"uid": 0, "temperature": 8 * B, "top_k": 12 * B, "top_p": 16 * B}
+             "top_p": dev_block[16 * B:20 * B].view(torch.float32),
+             "min_p": dev_block[20 * B:24 * B].view(torch.float32)}
+    offs = {"uid": 0, "temperature": 8 * B, "top_k": 12 * B, "top_p": 16 * B, "min_p": 20 * B}
     res = {}
-    for name in ("temperature", "top_k", "top_p", "uid"):
+    for name in ("temperature", "top_k", "top_p", "min_p", "uid"):
         ptr = getattr(out, name)
         if ptr is None:
             res[name] = None
@@ -320,9 +326,9 @@ class Sampler:
         self.handle = sampler_create(device, max_batch, vocab_size, dtype, seed)
 
     def prepare(self, B, temperature=None, top_k=None, top_p=None, uid=None, dev_block=None,
-                stream=None) -> dict:
+                stream=None, min_p=None) -> dict:
         return sampler_prepare(self.handle, B, temperature, top_k, top_p, uid, dev_block,
-                               stream=stream)
+                               stream=stream, min_p=min_p)
 
     def sample(self, logits, **kw) -> torch.Tensor:
         return sample_batch(self.handle, logits, **kw)

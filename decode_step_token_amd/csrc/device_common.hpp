@@ -105,16 +105,19 @@ struct RowParams {
     int k;        // effective top-k (V when disabled)
     float p;      // effective top-p (1 when disabled)
     bool top_p;   // p < 1
+    float min_p;  // effective min_p (0 when disabled)
 };
 
 // Sampler.prepare's per-request clamps, evaluated on the device.  A row is
 // greedy when its temperature is not above MIN_T (NaN included); top_k < 1
-// or >= V disables top-k; top_p is clamped to [MIN_P, 1] (NaN -> MIN_P).
+// or >= V disables top-k; top_p is clamped to [MIN_P, 1] (NaN -> MIN_P);
+// min_p (the pages' exercise) is off unless above 0 (NaN: off), at most 1.
 __device__ __forceinline__ RowParams row_params(const float* temperature, const int32_t* top_k,
-                                                const float* top_p, int b, int V) {
+                                                const float* top_p, const float* min_p, int b,
+                                                int V) {
     RowParams r;
     if (temperature == nullptr) {
-        r.greedy = true; r.T = kMinT; r.k = 1; r.p = 1.0f; r.top_p = false;
+        r.greedy = true; r.T = kMinT; r.k = 1; r.p = 1.0f; r.top_p = false; r.min_p = 0.0f;
         return r;
     }
     const float t = ld_global<float>(temperature + b);
@@ -126,7 +129,9 @@ __device__ __forceinline__ RowParams row_params(const float* temperature, const 
     p = fminf(fmaxf(p, kMinP), 1.0f);
     r.p = p;
     r.top_p = p < 1.0f;
-    if (r.greedy) { r.k = 1; r.top_p = false; }
+    const float mp = min_p ? ld_global<float>(min_p + b) : 0.0f;
+    r.min_p = mp > 0.0f ? fminf(mp, 1.0f) : 0.0f;
+    if (r.greedy) { r.k = 1; r.top_p = false; r.min_p = 0.0f; }
     return r;
 }
 

@@ -13,6 +13,9 @@
 //   4. top-p: the same radix descent weighted by mass: at each digit level it
 //      finds the bucket where the exclusive prefix mass crosses p * W_K, and
 //      finally how many equal-logit ties stay below the threshold;
+//   4b. min_p (the pages' exercise: p_i >= min_p * p_max on the full
+//      distribution, intersected with the top-k / top-p mask): the keys at
+//      or above m + T ln(min_p), a prefix too, so the shorter prefix stays;
 //   5. W = kept mass; the draw walks the row in token order in tiles,
 //      scanning per-thread partial sums, until the prefix exceeds u * W.
 // The kept set is always a prefix of the descending order, held as a cut
@@ -354,6 +357,15 @@ __device__ __noinline__ void exact_row(const SampleArgs& a, int b, const void* r
         });
         wk = block_sum<BLOCK>(wk, sm.dscr);
         cut = exact_cut_by_mass<DT, BLOCK>(row, V, cut, static_cast<double>(prm.p) * wk, m, prm.T, sm);
+    }
+
+    // 4b. min_p: p >= min_p * p_max, that is x >= m + T ln(min_p); its kept
+    // set is a prefix of the same order, so the intersection is the shorter
+    if (prm.min_p > 0.0f) {
+        const double xm = static_cast<double>(m) + static_cast<double>(prm.T) * log(static_cast<double>(prm.min_p));
+        const float xf = static_cast<float>(xm);
+        const uint32_t kmin = f32_key(xf) + (static_cast<double>(xf) < xm ? 1u : 0u);
+        if (cut.key < kmin) cut = Cut{kmin, INT64_MAX};
     }
 
     // 5. kept mass and size

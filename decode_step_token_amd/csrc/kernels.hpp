@@ -29,6 +29,7 @@ struct SampleArgs {
     const float* temperature;  // null: every row greedy
     const int32_t* top_k;      // may be null
     const float* top_p;        // may be null
+    const float* min_p;        // may be null
     const int64_t* uid;        // non-null unless temperature is null
     uint64_t step, seed;
     int32_t* tokens_out;

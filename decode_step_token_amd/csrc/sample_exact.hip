@@ -16,7 +16,7 @@ __global__ __launch_bounds__(kExactBlock) void sample_exact_kernel(SampleArgs a)
     __shared__ ExactSmem sm;
     const int b = blockIdx.x;
     const void* row = static_cast<const S*>(a.logits) + static_cast<int64_t>(b) * a.row_stride;
-    const RowParams prm = row_params(a.temperature, a.top_k, a.top_p, b, a.V);
+    const RowParams prm = row_params(a.temperature, a.top_k, a.top_p, a.min_p, b, a.V);
     const uint64_t word = request_word(a.seed, ld_global<int64_t>(a.uid + b), a.step);
     exact_row<DT, kExactBlock>(a, b, row, prm, word, uniform24(word), sm);
 }

@@ -106,6 +106,8 @@ struct Smem {
     unsigned long long mbest;     // merge: packed (key, ~index) maximum
     uint32_t mtotal, movf;        // merge: candidates stored, any region overflowed
     uint64_t word;                // the row's Philox word (written by wave 0)
+    float minp;                   // the row's effective min_p (0: off)
+    uint32_t kmin;                // min_p threshold as an order key (0: no min_p)
     double res_w;
     uint32_t res_token, res_kept;
     uint64_t wbest[kWaves];
@@ -487,19 +489,24 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);  // wave-uniform
     const void* row = static_cast<const S*>(a.logits) + static_cast<int64_t>(b) * a.row_stride;
-    const RowParams prm = row_params(a.temperature, a.top_k, a.top_p, b, V);
+    const RowParams prm = row_params(a.temperature, a.top_k, a.top_p, a.min_p, b, V);
     // The Philox word is wave-uniform scalar work (ten 64-bit multiply rounds);
     // only wave 0 uses it, so only wave 0 pays for it on the CU's scalar unit.
     uint64_t word = 0;
     if (wid == 0 && a.uid) word = request_word(a.seed, ld_global<int64_t>(a.uid + b), a.step);
-    if (threadIdx.x == 0) ss.word = word;   // for the other waves, after the next barrier
+    if (threadIdx.x == 0) {
+        ss.word = word;                     // for the other waves, after the next barrier
+        ss.minp = prm.min_p;
+    }
     const double u = uniform24(word);       // valid in wave 0
     const int n_tiles = (V + IO::TILE - 1) / IO::TILE;
 
+    // min_p alone is a value cut on the same candidates as top-p: such rows
+    // run as top-p rows (with p = 1)
     int mode;
     if (prm.greedy || prm.k == 1) mode = kArgmax;
     else if (prm.k < V) mode = kTopK;
-    else if (prm.top_p) mode = kTopP;
+    else if (prm.top_p || prm.min_p > 0.0f) mode = kTopP;
     else mode = kFull;
     const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
     // rows one read cannot serve go straight to the re-reading path
@@ -823,6 +830,19 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     const bool pre_ok = pre && (mode != kTopP ||
                                 (static_cast<double>(m) - static_cast<double>(m0)) * c <= 64.0);
     const double mc = mode == kTopP && pre_ok ? m0c : static_cast<double>(m) * c;
+    // min_p keeps p_i >= min_p * p_max, that is x >= m + T ln(min_p): the
+    // threshold in fp64, as the order key of the smallest float at or above
+    // it, kept in LDS (0: no min_p) and read where it is used
+    const bool has_min = mode != kArgmax && ss.minp > 0.0f;
+    if (has_min) {
+        if (threadIdx.x == 0) {
+            const double xm = static_cast<double>(m) + log2(static_cast<double>(ss.minp)) / c;
+            const float xf = static_cast<float>(xm);
+            ss.kmin = f32_key(xf) + (static_cast<double>(xf) < xm ? 1u : 0u);
+        }
+        __syncthreads();
+    }
+    auto kmin_now = [&]() -> uint32_t { return *reinterpret_cast<volatile uint32_t*>(&ss.kmin); };
     int32_t* topk_out = a.topk_idx_out ? a.topk_idx_out + static_cast<int64_t>(b) * kDebugTopK : nullptr;
 
     if (mode == kArgmax) {
@@ -1719,7 +1739,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 hsh = sh;
                 top_ext = false;
             }
-            int route = 0;           // 0 general, 1 S, 2 P, 3 finish from the row
+            int route = 0;           // 0 general, 1 S, 2 P, 3 finish from the row, 4 min_p list
             double ptgt = 0.0;       // top-p rows: p * Z
             BlockPick bp{};
             // the softmax normaliser of a top-p row (same value wherever it is used)
@@ -1736,11 +1756,29 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 else if (bp.above_c + bp.cnt <= static_cast<uint32_t>(kList)) route = 1;   // the whole nucleus listed
                 else if (bp.cnt <= static_cast<uint32_t>(kList)) route = 2;
             }
+            if (has_min && route != 1) {
+                // min_p rows that the small list does not finish: when every
+                // token min_p keeps is a candidate (and no top-p needs the
+                // mass of a top-k above kList), list the tokens at or above its
+                // threshold (route 4: route 1 over that list, if it holds at
+                // most kList); otherwise finish from the row
+                route = !small_k && kmin_now() >= lo && !(mode == kTopK && prm.top_p) ? 4 : 3;
+            }
             const uint32_t key_lo0 = lo;
             const uint32_t blo = key_lo0 + (bp.d >= 0 ? static_cast<uint32_t>(bp.d) << hsh : 0u);
             const uint32_t bhi = top_ext && bp.d == kBins - 1 ? key_hi : bin_hi(blo, static_cast<int>(hsh), key_hi);
-            if (route == 1) {
-                gather_pass(blo, key_hi, 0xffffffffu);
+            if (route == 1 || route == 4) {
+                gather_pass(route == 4 ? kmin_now() : blo, key_hi, 0xffffffffu);
+            }
+            if (route == 4 && ss.list_n > static_cast<uint32_t>(kList)) {
+                // more than kList tokens at or above the min_p threshold: the
+                // row path finishes the row
+                __syncthreads();
+                if (threadIdx.x == 0) ss.list_n = 0u;
+                __syncthreads();
+                route = 3;
+            }
+            if (route == 1 || route == 4) {
                 block_rank();
                 if (wid == 0) {
                     const int n = static_cast<int>(ss.list_n);
@@ -1751,13 +1789,18 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                     // top-k: the first k, then top-p inside them; top-p alone: the
                     // list holds every entry at or above the bin where the
                     // descending weight reaches p * Z
-                    const int k = mode == kTopK ? prm.k : n;
+                    const int k = mode == kTopK && prm.k < n ? prm.k : n;
                     int e = k - 1;
                     if (prm.top_p) {
                         const double target_p = mode == kTopK
                             ? static_cast<double>(prm.p) * readlane_f64(incl, k - 1) : ptgt;
                         const uint64_t bal = __ballot(lane < k && incl >= target_p);
                         if (bal) e = __ffsll(static_cast<unsigned long long>(bal)) - 1;
+                    }
+                    if (has_min) {
+                        // min_p's prefix: the listed entries at or above kmin
+                        const int em = __popcll(__ballot(in && ss.skey[lane] >= kmin_now())) - 1;
+                        e = em < e ? em : e;
                     }
                     const uint32_t ck = readlane_u32(in ? ss.skey[lane] : 0u, e);
                     const uint32_t cl = readlane_u32(in ? ss.sidx[lane] : 0u, e);
@@ -1806,7 +1849,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 __syncthreads();
                 block_tile_draw(Cut{ss.cut_key, ss.cut_last});
             }
-            if (route == 1 || route == 2) {
+            if (route == 1 || route == 2 || route == 4) {
                 fast = true;
                 cut = Cut{ss.cut_key, ss.cut_last};
                 token = ss.res_token;
@@ -1856,7 +1899,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     // entries of that bin gathered into the LDS regions.  The cut inside the
     // bin is then the mass descent over LDS entries, and the draw scans the
     // per-tile kept weights and reads the chosen tile once more.
-    if (!fast && mode == kTopP && want_lanez && aligned) {
+    if (!fast && mode == kTopP && want_lanez && aligned && !has_min) {
         constexpr int kTS = __builtin_ctz(IO::TILE);
         __syncthreads();                       // every wave's share of Z is in ss.wd
         double z = 0.0;
@@ -2078,6 +2121,12 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 cut = pc;
                 have_w = true;
             }
+        }
+        // min_p's kept set is a prefix too, so the intersection is the shorter
+        // prefix: it binds when the cut so far keeps keys below its threshold
+        if (has_min && cut.key < kmin_now()) {
+            cut = Cut{kmin_now(), 0xffffffffu};
+            have_w = false;
         }
 
         // ---- the draw: first index (token order) whose kept prefix exceeds u*W --

@@ -196,7 +196,8 @@ int sampler_create(dst_sampler** out, int device, int32_t max_batch, int32_t voc
 
 int sample_batch(dst_sampler* s, void* stream, const void* logits, int64_t row_stride, int32_t B,
                  const float* temperature, const int32_t* top_k, const float* top_p,
-                 const int64_t* uid, uint64_t step, int32_t* tokens_out, const sampler_debug* dbg) {
+                 const float* min_p, const int64_t* uid, uint64_t step, int32_t* tokens_out,
+                 const sampler_debug* dbg) {
     if (!s) return SAMPLER_EINVAL;
     if (B < 0 || B > s->max_batch) return fail(s, SAMPLER_EINVAL, "sample_batch: B out of range");
     if (B == 0) return SAMPLER_OK;
@@ -232,6 +233,7 @@ int sample_batch(dst_sampler* s, void* stream, const void* logits, int64_t row_s
         a.temperature = temperature;
         a.top_k = top_k;
         a.top_p = top_p;
+        a.min_p = min_p;
         a.uid = uid;
         a.step = step;
         a.seed = s->seed;
@@ -305,11 +307,11 @@ int gather_tokens(dst_sampler* s, void* stream, const int32_t* token_pool, int64
 }
 
 int sampler_prepare(dst_sampler* s, void* stream, int32_t B, const float* temperature,
-                    const int32_t* top_k, const float* top_p, const int64_t* uid, void* dev_block,
-                    int64_t block_bytes, sampler_args* out) {
+                    const int32_t* top_k, const float* top_p, const float* min_p,
+                    const int64_t* uid, void* dev_block, int64_t block_bytes, sampler_args* out) {
     if (!s) return SAMPLER_EINVAL;
     if (!out) return fail(s, SAMPLER_EINVAL, "sampler_prepare: null out");
-    *out = sampler_args{nullptr, nullptr, nullptr, nullptr, B};
+    *out = sampler_args{nullptr, nullptr, nullptr, nullptr, nullptr, B};
     if (B < 0 || B > s->max_batch) return fail(s, SAMPLER_EINVAL, "sampler_prepare: B out of range");
     // a request is greedy iff its temperature is <= 0 (NaN is not)
     bool all_greedy = true;
@@ -332,11 +334,12 @@ int sampler_prepare(dst_sampler* s, void* stream, int32_t B, const float* temper
     float* h_t = reinterpret_cast<float*>(h + 8 * static_cast<size_t>(B));
     int32_t* h_k = reinterpret_cast<int32_t*>(h + 12 * static_cast<size_t>(B));
     float* h_p = reinterpret_cast<float*>(h + 16 * static_cast<size_t>(B));
+    float* h_m = reinterpret_cast<float*>(h + 20 * static_cast<size_t>(B));
     // the pages' values, in double as Python computes them, stored as fp32;
     // max(a, b) and min(a, b) keep their first argument unless the second is
     // strictly larger (smaller), as Python's do
     const double kMin = 1e-6;
-    bool any_k = false, any_p = false;
+    bool any_k = false, any_p = false, any_m = false;
     for (int32_t b = 0; b < B; ++b) {
         const double t = temperature[b] <= 0.0f ? 0.0 : static_cast<double>(temperature[b]);
         h_t[b] = static_cast<float>(kMin > t ? kMin : t);
@@ -348,6 +351,8 @@ int sampler_prepare(dst_sampler* s, void* stream, int32_t B, const float* temper
         const double p2 = 1.0 < p1 ? 1.0 : p1;
         h_p[b] = static_cast<float>(p2);
         any_p = any_p || p2 < 1.0;
+        h_m[b] = min_p ? min_p[b] : 0.0f;
+        any_m = any_m || h_m[b] > 0.0f;
         h_uid[b] = uid[b];
     }
     // the upload is a kernel reading the staging buffer through its mapping
@@ -365,6 +370,7 @@ int sampler_prepare(dst_sampler* s, void* stream, int32_t B, const float* temper
     out->temperature = reinterpret_cast<const float*>(d + 8 * static_cast<size_t>(B));
     out->top_k = any_k ? reinterpret_cast<const int32_t*>(d + 12 * static_cast<size_t>(B)) : nullptr;
     out->top_p = any_p ? reinterpret_cast<const float*>(d + 16 * static_cast<size_t>(B)) : nullptr;
+    out->min_p = any_m ? reinterpret_cast<const float*>(d + 20 * static_cast<size_t>(B)) : nullptr;
     return SAMPLER_OK;
 }
 

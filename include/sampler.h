@@ -110,7 +110,7 @@ typedef struct sampler_debug {
  *   logits_dtype SAMPLER_F32 or SAMPLER_BF16 (raw bf16 bit patterns).
  *   seed        key of the counter-based generator (the engine seeds with 42).
  * Allocates the device workspace (hipMalloc), the pinned staging buffers
- * (hipHostMalloc, SAMPLER_PREP_SLOTS x (20 + 32) x max_batch bytes) and
+ * (hipHostMalloc, SAMPLER_PREP_SLOTS x (24 + 32) x max_batch bytes) and
  * events; the only call that allocates.  Errors: SAMPLER_EINVAL,
  * SAMPLER_ENOMEM, SAMPLER_EHIP.
  */
@@ -137,6 +137,12 @@ DST_API int sampler_destroy(dst_sampler* s);
  *               1 disables.  top-k is applied first, then top-p on the
  *               renormalised survivors; a rank is kept while the mass before
  *               it is < top_p, so the most likely token is always kept.
+ *   min_p       dev [B] fp32 or NULL (disabled); the pages' exercise
+ *               ("The engine and the sampler", section "Exercises"): keep
+ *               the tokens whose probability (temperature applied, full
+ *               distribution) is at least min_p times the largest, and
+ *               intersect that with the top-k / top-p set.  A value not
+ *               above 0 (or NaN) disables it; values above 1 act as 1.
  *   uid         dev [B] int64 request ids; required when temperature != NULL.
  *   step        decode-step counter.  The row's uniform u comes from
  *               Philox-4x64-10 with key (seed, 0) and counter
@@ -150,8 +156,8 @@ DST_API int sampler_destroy(dst_sampler* s);
  */
 DST_API int sample_batch(dst_sampler* s, void* stream, const void* logits, int64_t row_stride,
                  int32_t B, const float* temperature, const int32_t* top_k,
-                 const float* top_p, const int64_t* uid, uint64_t step, int32_t* tokens_out,
-                 const sampler_debug* dbg);
+                 const float* top_p, const float* min_p, const int64_t* uid, uint64_t step,
+                 int32_t* tokens_out, const sampler_debug* dbg);
 
 /*
  * write_tokens -- token_pool[rows[b], cols[b]] = tokens[b], then an async copy
@@ -243,39 +249,44 @@ DST_API int write_page_table(dst_sampler* s, void* stream, int32_t* page_table,
  *               (sample_batch then takes the plain argmax path).
  *   top_k       host [B] int32, or NULL (no request sets it).
  *   top_p       host [B] fp32, or NULL (no request sets it).
+ *   min_p       host [B] fp32, or NULL (no request sets it).
  *   uid         host [B] int64; required unless every request is greedy.
  *   dev_block   dev, caller-owned, 8-byte aligned, at least
  *               SAMPLER_PREP_BYTES(B) bytes; receives, packed:
- *               uid int64[B] | temperature fp32[B] | top_k int32[B] | top_p fp32[B]
+ *               uid int64[B] | temperature fp32[B] | top_k int32[B] |
+ *               top_p fp32[B] | min_p fp32[B]
  *               with the pages' values: temperature max(0 if greedy else T,
  *               1e-6); top_k k if k >= 1 else vocab_size; top_p
  *               min(max(p, 1e-6), 1) (each computed in double, stored
- *               rounded to fp32).  The caller must not reuse it before the
+ *               rounded to fp32); min_p as given (0 where not set).  The caller must not reuse it before the
  *               sample_batch that reads it has run (stream order suffices).
  *   out         host: device pointers into dev_block for sample_batch, each
  *               NULL where the pages pass None: temperature (all greedy),
  *               top_k (every entry equals vocab_size), top_p (no entry
- *               below 1); uid NULL with temperature.
+ *               below 1), min_p (no entry above 0); uid NULL with
+ *               temperature.
  * The host arrays are read before the call returns (pageable memory is
  * fine).  The library keeps SAMPLER_PREP_SLOTS pinned staging buffers in
  * rotation; a call waits on the host only if the upload issued from the same
  * buffer that many calls earlier has not finished.
  * Errors: SAMPLER_EINVAL (synchronous, nothing enqueued); SAMPLER_EHIP.
  */
-#define SAMPLER_PREP_BYTES(B) ((int64_t)(B) * 20)
+#define SAMPLER_PREP_BYTES(B) ((int64_t)(B) * 24)
 #define SAMPLER_PREP_SLOTS 8
 
 typedef struct sampler_args {
     const float*   temperature;
     const int32_t* top_k;
     const float*   top_p;
+    const float*   min_p;
     const int64_t* uid;
     int32_t        B;
 } sampler_args;
 
 DST_API int sampler_prepare(dst_sampler* s, void* stream, int32_t B, const float* temperature,
-                            const int32_t* top_k, const float* top_p, const int64_t* uid,
-                            void* dev_block, int64_t block_bytes, sampler_args* out);
+                            const int32_t* top_k, const float* top_p, const float* min_p,
+                            const int64_t* uid, void* dev_block, int64_t block_bytes,
+                            sampler_args* out);
 
 /*
  * sampler_wait -- block until the ticket's work (and its host copy) is done:

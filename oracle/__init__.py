@@ -18,6 +18,11 @@ Pins (each in ``tests/test_oracle_pins.py``):
   round trip, and the packed positions of a hand-worked prefill + decode batch.
 * ``prepare``: hand-worked batches (clamps and the None rules), and that the
   per-row routing of the prepared tensors equals that of the raw parameters.
+* ``min_p_count`` (min_p in ``sample_row``): the pages' worked logits give
+  the closed forms of top-k 2 at min_p 0.2; min_p 1 is argmax (all ties at
+  the maximum kept); the prefix-minimum equals the literal intersection of
+  the masks by brute force; the count equals the logit-space threshold
+  ``x >= m + T ln(min_p)``; min_p 0 changes nothing.
 * ``PagePool`` / ``paged_info`` / ``page_to_token`` / ``write_page_table``:
   the pages' page-aligned allocation test (row [0..7], free pages 6, 6, 5, a
   new page starting at a multiple of 4), their worked page count (page size
@@ -26,14 +31,16 @@ Pins (each in ``tests/test_oracle_pins.py``):
   twice).
 """
 from .philox import philox4x64, request_uniform, request_word, uniform24
-from .sampler_ref import (CUT_BAND, DRAW_BAND, MIN_P, MIN_T, RowParams, RowResult,
+from .sampler_ref import (CUT_BAND, DRAW_BAND, MIN_P, MIN_P_BAND, MIN_T, RowParams, RowResult,
                           descending_order, filter_sorted, gather_tokens, input_tuple,
-                          inverse_cdf, PagePool, page_to_token, paged_info, prepare,
+                          inverse_cdf, min_p_count, PagePool, page_to_token, paged_info,
+                          prepare,
                           row_params, sample_batch, sample_row, widen_logits,
                           write_page_table, write_tokens)
 
 __all__ = [
     "philox4x64", "request_uniform", "request_word", "uniform24", "CUT_BAND", "DRAW_BAND",
+    "MIN_P_BAND", "min_p_count",
     "MIN_P", "MIN_T", "RowParams", "RowResult", "descending_order", "filter_sorted",
     "gather_tokens", "input_tuple", "inverse_cdf", "PagePool", "page_to_token", "paged_info",
     "prepare", "write_page_table", "row_params", "sample_batch", "sample_row", "widen_logits", "write_tokens",

@@ -53,6 +53,7 @@ MIN_T = float(np.float32(1e-6))
 MIN_P = float(np.float32(1e-6))
 DRAW_BAND = 1e-5
 CUT_BAND = 1e-6
+MIN_P_BAND = 1e-9      # min_p: |log(p_i / p_max) - log(min_p)| below this is ambiguous
 
 
 def widen_logits(logits: np.ndarray, dtype: str) -> np.ndarray:
@@ -70,10 +71,15 @@ class RowParams:
     T: float          # effective temperature (float32 value, widened)
     k: int            # effective top-k (V when disabled)
     p: float          # effective top-p (1.0 when disabled)
+    min_p: float = 0.0  # effective min_p (0.0 when disabled)
 
 
-def row_params(V: int, T: Optional[float], k: Optional[int], p: Optional[float]) -> RowParams:
-    """``Sampler.prepare``'s clamps for one request, evaluated in float32."""
+def row_params(V: int, T: Optional[float], k: Optional[int], p: Optional[float],
+               min_p: Optional[float] = None) -> RowParams:
+    """``Sampler.prepare``'s clamps for one request, evaluated in float32.
+    min_p (the pages' exercise, "The engine and the sampler", section
+    "Exercises"): a value not above 0 (or NaN) disables it, values above 1
+    act as 1."""
     if T is None:
         return RowParams(True, MIN_T, 1, 1.0)
     t32 = np.float32(T)
@@ -86,7 +92,11 @@ def row_params(V: int, T: Optional[float], k: Optional[int], p: Optional[float])
         p32 = np.float32(p)
         p_eff = float(p32) if p32 > np.float32(MIN_P) else MIN_P
         p_eff = min(p_eff, 1.0)
-    return RowParams(greedy, T_eff, k_eff, p_eff)
+    mp_eff = 0.0
+    if min_p is not None:
+        m32 = np.float32(min_p)
+        mp_eff = min(float(m32), 1.0) if m32 > 0 else 0.0
+    return RowParams(greedy, T_eff, k_eff, p_eff, mp_eff)
 
 
 def descending_order(x: np.ndarray) -> np.ndarray:
@@ -118,6 +128,18 @@ def filter_sorted(q_sorted: np.ndarray, k: int, p: float, order: str = "k_then_p
             n = int(np.count_nonzero(before < p))
         return min(n, k)
     raise ValueError(order)
+
+
+def min_p_count(q_sorted: np.ndarray, min_p: float) -> int:
+    """Length of the prefix kept by min_p: the tokens whose probability is at
+    least the maximum probability times min_p ("The engine and the sampler",
+    section "Exercises", exercise 2 and its answer: the mask is taken on the
+    full temperature-scaled distribution and intersected with the top-k /
+    top-p mask; both masks are prefixes of the descending order, so the
+    intersection is the shorter prefix)."""
+    if min_p <= 0.0:
+        return len(q_sorted)
+    return int(np.count_nonzero(q_sorted >= q_sorted[0] * min_p))
 
 
 def inverse_cdf(r: np.ndarray, u: float) -> int:
@@ -181,23 +203,40 @@ def sample_row(x: np.ndarray, params: RowParams, u: float, word0: int = 0,
     w = np.exp((x - m) / params.T)          # softmax(logits / T), max subtracted
     prob = w / w.sum()
     q_sorted = prob[pi]
-    n = filter_sorted(q_sorted, params.k, params.p, order)
+    n_kp = filter_sorted(q_sorted, params.k, params.p, order)
+    n_min = min_p_count(q_sorted, params.min_p)
+    n = min(n_kp, n_min)
     r = _distribution(x, params.T, pi, n)
     tok = inverse_cdf(r, u)
     res = RowResult(tok, False, r, n, pi[:min(params.k, 64)].copy(), u, word0, params)
     res.draw_ambiguous, res.acceptable = _acceptable(r, u)
 
-    if order == "k_then_p" and params.p < 1.0 and want_alternatives:
+    if not want_alternatives:
+        return res
+    # kept lengths that rounding at a cut-off may also give
+    kp_alts = {n_kp}
+    if order == "k_then_p" and params.p < 1.0:
         k = min(params.k, V)
         q = q_sorted[:k] / q_sorted[:k].sum()
         before = np.concatenate(([0.0], np.cumsum(q)[:-1]))
         if np.any(np.abs(before - params.p) < CUT_BAND):
-            res.cutoff_ambiguous = True
-            for n_alt in (n - 1, n + 1):
-                if 1 <= n_alt <= k:
-                    r_alt = _distribution(x, params.T, pi, n_alt)
-                    res.alt_r[n_alt] = r_alt
-                    res.alt_acceptable[n_alt] = _acceptable(r_alt, u)[1] + [inverse_cdf(r_alt, u)]
+            kp_alts |= {a for a in (n_kp - 1, n_kp + 1) if 1 <= a <= k}
+    min_alts = {n_min}
+    if params.min_p > 0.0:
+        # distance to the min_p threshold in log-probability
+        d = (x[pi] - m) / params.T - np.log(params.min_p)
+        near = np.abs(d) < MIN_P_BAND
+        if np.any(near):
+            min_alts |= {int(np.count_nonzero(d > MIN_P_BAND)),
+                         int(np.count_nonzero(d >= -MIN_P_BAND))}
+    alts = {min(a, b) for a in kp_alts for b in min_alts} - {n}
+    alts = {a for a in alts if a >= 1}
+    if alts:
+        res.cutoff_ambiguous = True
+        for n_alt in sorted(alts):
+            r_alt = _distribution(x, params.T, pi, n_alt)
+            res.alt_r[n_alt] = r_alt
+            res.alt_acceptable[n_alt] = _acceptable(r_alt, u)[1] + [inverse_cdf(r_alt, u)]
     return res
 
 
@@ -208,13 +247,14 @@ def _opt(a: Optional[np.ndarray], b: int):
 def sample_batch(logits: np.ndarray, dtype: str, temperature: Optional[np.ndarray],
                  top_k: Optional[np.ndarray], top_p: Optional[np.ndarray],
                  uid: np.ndarray, step: int, seed: int, rows=None,
-                 order: str = "k_then_p") -> List[RowResult]:
+                 order: str = "k_then_p", min_p: Optional[np.ndarray] = None) -> List[RowResult]:
     """Every request of one decode step (or the subset ``rows``)."""
     X = widen_logits(logits, dtype)
     B, V = X.shape
     out = []
     for b in (range(B) if rows is None else rows):
-        prm = row_params(V, _opt(temperature, b), _opt(top_k, b), _opt(top_p, b))
+        prm = row_params(V, _opt(temperature, b), _opt(top_k, b), _opt(top_p, b),
+                         _opt(min_p, b))
         if temperature is None:
             u, w0 = 0.0, 0
         else:
@@ -274,32 +314,41 @@ def input_tuple(table_idx, cached_len, device_len):
     return np.asarray(rows, dtype=np.int64), np.asarray(pos, dtype=np.int64)
 
 
-def prepare(V: int, temperature, top_k, top_p):
+def prepare(V: int, temperature, top_k, top_p, min_p=None):
     """``Sampler.prepare`` for a batch ("The engine and the sampler", section
     "The sampler"), from request-level parameters (each array may be None:
     not set by any request).  A request is greedy iff its temperature is
     <= 0.  The values are computed on Python floats as the pages do, then
     stored as float32 / int32.
 
-    Returns (temperature, top_k, top_p): float32 / int32 / float32 arrays, or
-    None where the pages pass None."""
+    min_p (the pages' exercise) follows the same rule: a tensor only when
+    some request sets a value above 0; the value is passed as given and
+    clamped where it is used.
+
+    Returns (temperature, top_k, top_p), or (temperature, top_k, top_p,
+    min_p) when ``min_p`` is given: float32 / int32 / float32 (/ float32)
+    arrays, or None where the pages pass None."""
     B = 0
-    for a in (temperature, top_k, top_p):
+    for a in (temperature, top_k, top_p, min_p):
         if a is not None:
             B = len(a)
     T = [0.0] * B if temperature is None else [float(np.float32(t)) for t in temperature]
     greedy = [not (t > 0.0) if t == t else False for t in T]       # NaN is not greedy
     if all(greedy):
-        return None, None, None
-    min_t = min_p = 1e-6
+        return (None, None, None) if min_p is None else (None, None, None, None)
+    min_t = min_p_clamp = 1e-6
     ts = [max(0.0 if g else t, min_t) for g, t in zip(greedy, T)]
     ks_in = [-1] * B if top_k is None else [int(k) for k in top_k]
     ks = [k if k >= 1 else V for k in ks_in]
     ps_in = [1.0] * B if top_p is None else [float(np.float32(p)) for p in top_p]
-    ps = [min(max(p, min_p), 1.0) for p in ps_in]
+    ps = [min(max(p, min_p_clamp), 1.0) for p in ps_in]
     out_k = np.array(ks, dtype=np.int32) if any(k != V for k in ks) else None
     out_p = np.array(ps, dtype=np.float32) if any(p < 1.0 for p in ps) else None
-    return np.array(ts, dtype=np.float32), out_k, out_p
+    if min_p is None:
+        return np.array(ts, dtype=np.float32), out_k, out_p
+    mps = [float(np.float32(v)) for v in min_p]
+    out_m = np.array(mps, dtype=np.float32) if any(v > 0.0 for v in mps) else None
+    return np.array(ts, dtype=np.float32), out_k, out_p, out_m
 
 
 def _div_ceil(a: int, b: int) -> int:

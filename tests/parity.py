@@ -65,7 +65,7 @@ def run_gpu(w: Workload, sampler: dst.Sampler = None, debug: bool = True, pad: i
         if force_exact:
             dbg = dict(dbg or {}, force_exact=True)
         toks = sampler.sample(logits, temperature=T, top_k=k, top_p=p, uid=uid, step=w.step,
-                              debug=dbg)
+                              debug=dbg, min_p=opt(w.min_p, torch.float32))
         pool = torch.from_numpy(w.pool.copy()).cuda()
         rows = opt(w.rows, torch.int64)
         cols = opt(w.cols, torch.int64)
@@ -86,7 +86,7 @@ def run_gpu(w: Workload, sampler: dst.Sampler = None, debug: bool = True, pad: i
 
 def run_oracle(w: Workload, rows=None):
     return oracle.sample_batch(w.logits, w.dtype, w.temperature, w.top_k, w.top_p, w.uid,
-                               w.step, w.seed, rows=rows)
+                               w.step, w.seed, rows=rows, min_p=w.min_p)
 
 
 def compare(w: Workload, gpu: dict, ref, rows=None, check_probs_rows=None) -> dict:

@@ -137,7 +137,8 @@ def _overlap_loop(s, w0, logits_dev, steps, debug):
     out_pos = [_dev(pos0 + st) for st in range(steps)]
     # the parameters are prepared every step from host arrays, as the
     # scheduler does; two device blocks alternate
-    blocks = [torch.empty(20 * B, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    blocks = [torch.empty(dst._binding.PREP_BYTES_PER_REQUEST * B, dtype=torch.uint8,
+                          device="cuda") for _ in range(2)]
     ring = [torch.full((B,), -7, dtype=torch.int32).pin_memory() for _ in range(2)]
     ids = [torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(steps)]
     toks = [torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(steps)]

@@ -1,0 +1,74 @@
+"""min_p (the pages' exercise: keep p_i >= min_p * p_max on the full
+temperature-scaled distribution, intersected with the top-k / top-p set),
+through the C ABI, against the fp64 oracle on every row."""
+import numpy as np
+import pytest
+import torch
+
+import decode_step_token_amd as dst
+import workloads as wl
+from tests.parity import compare, log, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+MIN_P_VALUES = [0.0, -1.0, 0.01, 0.05, 0.2, 0.5, 1.0, 1.5]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    dst.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _check(w, **kw):
+    log(f"case {w.name} B={w.B} V={w.V} dtype={w.dtype} "
+        f"{'exact path' if kw.get('force_exact') else ''}")
+    gpu = run_gpu(w, **kw)
+    stats = compare(w, gpu, run_oracle(w))
+    log(f"  ok {stats}")
+    return gpu
+
+
+@pytest.mark.parametrize("V,dtype,seed", [(64, "f32", 1), (1000, "bf16", 2), (5000, "f32", 3),
+                                          (33000, "bf16", 4), (151936, "f32", 5)])
+def test_tiny_batches(V, dtype, seed):
+    rng = np.random.default_rng(seed)
+    w = wl.with_min_p(wl.tiny(rng, 48, V, dtype), MIN_P_VALUES, seed)
+    _check(w)
+
+
+@pytest.mark.parametrize("V,dtype,seed", [(1000, "f32", 6), (33000, "bf16", 7)])
+def test_exact_path(V, dtype, seed):
+    rng = np.random.default_rng(seed)
+    w = wl.with_min_p(wl.tiny(rng, 32, V, dtype), MIN_P_VALUES, seed)
+    _check(w, force_exact=True)
+
+
+def test_c3_with_min_p():
+    """c3's parameter mix with min_p from {0, 0.02, 0.05, 0.1}: the kept set
+    is mostly min_p's own (a few tokens), listed from the candidates."""
+    w = wl.with_min_p(wl.c3(), [0.0, 0.02, 0.05, 0.1], 8)
+    _check(w)
+
+
+def test_flat_rows_min_p_only():
+    """c3 logits at T = 1.5 with min_p alone: small min_p keeps thousands of
+    tokens (finished from the row), larger ones a few (listed)."""
+    w = wl.c3()
+    B = 64
+    w = wl.Workload("c3_T1.5_min_p", w.dtype, w.logits[:B].copy(),
+                    np.full(B, 1.5, np.float32), None, None, w.uid[:B].copy(), 3,
+                    w.pool[:B].copy(), np.arange(B, dtype=np.int64), w.cols[:B].copy())
+    w = wl.with_min_p(w, [0.001, 0.01, 0.1, 0.5], 9)
+    _check(w)
+
+
+def test_min_p_zero_changes_nothing():
+    rng = np.random.default_rng(10)
+    w = wl.tiny(rng, 64, 20000, "f32")
+    log(f"case min_p all zero on {w.name}")
+    a = run_gpu(w, debug=False)
+    b = run_gpu(wl.with_min_p(w, [0.0], 0), debug=False)
+    assert np.array_equal(a["tokens"], b["tokens"])

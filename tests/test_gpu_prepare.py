@@ -28,8 +28,9 @@ def _params(rng, B, V):
     T = rng.choice(np.array([0.0, -1.0, np.nan, 1e-9, 1e-6, 0.3, 0.7, 1.5], np.float32), B)
     k = rng.choice(np.array([-3, 0, 1, 2, 50, V - 1, V, V + 4], np.int32), B)
     p = rng.choice(np.array([1e-12, 1e-6, 0.5, 0.9, 1.0, 2.0], np.float32), B)
+    mp = rng.choice(np.array([0.0, 0.0, -0.5, 0.05, 0.3, 1.0, 3.0], np.float32), B)
     uid = rng.integers(-(1 << 40), 1 << 40, B).astype(np.int64)
-    return T, k, p, uid
+    return T, k, p, mp, uid
 
 
 def _same(got, want, name):
@@ -51,16 +52,19 @@ def _same(got, want, name):
 def test_prepare_matches_oracle(B, V, seed):
     log(f"case prepare B={B} V={V}")
     rng = np.random.default_rng(seed)
-    T, k, p, uid = _params(rng, B, V)
+    T, k, p, mp, uid = _params(rng, B, V)
     T[0] = 0.5                                 # at least one sampled request
     with dst.Sampler(0, B, V) as s:
-        got = s.prepare(B, T, k, p, uid)
+        got = s.prepare(B, T, k, p, uid, min_p=mp)
+        nomp = s.prepare(B, T, k, p, uid)
         torch.cuda.synchronize()
-    ts, ks, ps = oracle.prepare(V, T, k, p)
-    _same(got["temperature"], ts, "temperature")
-    _same(got["top_k"], ks, "top_k")
-    _same(got["top_p"], ps, "top_p")
-    assert np.array_equal(got["uid"].cpu().numpy(), uid)
+        ts, ks, ps, ms = oracle.prepare(V, T, k, p, mp)
+        _same(got["temperature"], ts, "temperature")
+        _same(got["top_k"], ks, "top_k")
+        _same(got["top_p"], ps, "top_p")
+        _same(got["min_p"], ms, "min_p")
+        assert np.array_equal(got["uid"].cpu().numpy(), uid)
+        assert nomp["min_p"] is None
 
 
 def test_prepare_none_rules_and_errors():
@@ -84,17 +88,17 @@ def test_prepare_none_rules_and_errors():
         uh = torch.from_numpy(uid)
         vp = lambda t: ctypes.c_void_p(t.data_ptr())
         # B above max_batch, uid missing, block too small, misaligned block
-        assert lib.sampler_prepare(s.handle, None, 9, None, None, None, None, vp(blk), 64,
+        assert lib.sampler_prepare(s.handle, None, 9, None, None, None, None, None, vp(blk), 64,
                                    ctypes.byref(out)) == -1
-        assert lib.sampler_prepare(s.handle, None, 2, vp(Th), None, None, None, vp(blk), 64,
-                                   ctypes.byref(out)) == -1
-        assert lib.sampler_prepare(s.handle, None, 2, vp(Th), None, None, vp(uh), vp(blk), 39,
-                                   ctypes.byref(out)) == -1
-        assert lib.sampler_prepare(s.handle, None, 2, vp(Th), None, None, vp(uh),
+        assert lib.sampler_prepare(s.handle, None, 2, vp(Th), None, None, None, None, vp(blk),
+                                   64, ctypes.byref(out)) == -1
+        assert lib.sampler_prepare(s.handle, None, 2, vp(Th), None, None, None, vp(uh), vp(blk),
+                                   47, ctypes.byref(out)) == -1
+        assert lib.sampler_prepare(s.handle, None, 2, vp(Th), None, None, None, vp(uh),
                                    ctypes.c_void_p(blk.data_ptr() + 4), 60,
                                    ctypes.byref(out)) == -1
-        assert lib.sampler_prepare(s.handle, None, 2, vp(Th), None, None, vp(uh), vp(blk), 40,
-                                   None) == -1
+        assert lib.sampler_prepare(s.handle, None, 2, vp(Th), None, None, None, vp(uh), vp(blk),
+                                   48, None) == -1
         s.check()
 
 
@@ -121,27 +125,30 @@ def test_prepare_staging_rotation_under_load():
     log(f"case prepare staging rotation, {n} calls")
     rng = np.random.default_rng(11)
     sets = [_params(rng, B, V) for _ in range(n)]
-    for T, _, _, _ in sets:
+    for T, *_ in sets:
         T[0] = 0.8
     logits = torch.from_numpy(rng.standard_normal((B, V)).astype(np.float32)).cuda()
     with dst.Sampler(0, B, V) as s:
-        blocks = [torch.empty(20 * B, dtype=torch.uint8, device="cuda") for _ in range(n)]
+        blocks = [torch.empty(dst._binding.PREP_BYTES_PER_REQUEST * B, dtype=torch.uint8,
+                              device="cuda") for _ in range(n)]
         toks = [torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(n)]
         got = []
         torch.cuda._sleep(int(2e6))            # keep the stream busy while calls pile up
-        for i, (T, k, p, uid) in enumerate(sets):
-            g = s.prepare(B, T, k, p, uid, dev_block=blocks[i])
+        for i, (T, k, p, mp, uid) in enumerate(sets):
+            g = s.prepare(B, T, k, p, uid, dev_block=blocks[i], min_p=mp)
             s.sample(logits, step=i, tokens_out=toks[i], **g)
             got.append(g)
         torch.cuda.synchronize()
-        for i, (T, k, p, uid) in enumerate(sets):
-            ts, ks, ps = oracle.prepare(V, T, k, p)
+        for i, (T, k, p, mp, uid) in enumerate(sets):
+            ts, ks, ps, ms = oracle.prepare(V, T, k, p, mp)
             _same(got[i]["temperature"], ts, f"call {i} temperature")
             _same(got[i]["top_k"], ks, f"call {i} top_k")
             _same(got[i]["top_p"], ps, f"call {i} top_p")
+            _same(got[i]["min_p"], ms, f"call {i} min_p")
             ref = s.sample(logits, step=i, temperature=torch.from_numpy(ts).cuda(),
                            top_k=None if ks is None else torch.from_numpy(ks).cuda(),
                            top_p=None if ps is None else torch.from_numpy(ps).cuda(),
+                           min_p=None if ms is None else torch.from_numpy(ms).cuda(),
                            uid=torch.from_numpy(uid).cuda())
             assert torch.equal(ref, toks[i]), f"call {i}: tokens"
         s.check()

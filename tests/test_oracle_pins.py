@@ -18,8 +18,8 @@ import scipy.stats
 import oracle
 from oracle import (filter_sorted, inverse_cdf, philox4x64, request_uniform, request_word,
                     row_params, sample_batch, sample_row, widen_logits, write_tokens)
-from oracle import (PagePool, gather_tokens, input_tuple, page_to_token, paged_info, prepare,
-                    write_page_table)
+from oracle import (PagePool, gather_tokens, input_tuple, min_p_count, page_to_token, paged_info,
+                    prepare, write_page_table)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 M64 = (1 << 64) - 1
@@ -458,6 +458,71 @@ def test_prepare_keeps_every_rows_routing():
         prep = row_params(V, float(ts[b]), None if ks is None else int(ks[b]),
                           None if ps is None else float(ps[b]))
         assert raw == prep, (b, T[b], k[b], p[b])
+
+
+# -------------------------------------------------------------- min_p ---
+
+def test_min_p_on_the_pages_logits():
+    """The pages' worked logits [5, 4, 3, 0, 0, 0] at T = 1: probabilities
+    relative to the maximum are 1, 1/e, 1/e^2, 1/e^5 ... min_p 0.2 keeps
+    {0, 1} (as top-k 2: token 0 with probability e/(1+e)), min_p 0.1 keeps
+    {0, 1, 2}, min_p 1 keeps the maximum only."""
+    x = np.array([5.0, 4.0, 3.0, 0.0, 0.0, 0.0])
+    e = np.e
+    for mp, kept, r0 in ((0.2, 2, e / (1 + e)), (0.1, 3, e * e / (e * e + e + 1)), (1.0, 1, 1.0),
+                         (np.exp(-5) * 0.999, 6, None)):
+        prm = row_params(6, 1.0, -1, 1.0, mp)
+        res = sample_row(x, prm, 0.5)
+        assert res.kept == kept, mp
+        if r0 is not None:
+            assert abs(res.r[0] - r0) < 1e-15
+    # min_p 1 with a tie at the maximum keeps both maxima
+    res = sample_row(np.array([2.0, 7.0, 7.0, 1.0]), row_params(4, 0.5, -1, 1.0, 1.0), 0.7)
+    assert res.kept == 2 and set(np.flatnonzero(res.r)) == {1, 2}
+
+
+def test_min_p_is_the_intersection_of_masks():
+    """By brute force: the kept set equals (top-k then top-p mask) AND
+    (p_i >= p_max * min_p), computed on token indices."""
+    rng = np.random.default_rng(14)
+    for _ in range(300):
+        V = int(rng.integers(2, 9))
+        x = np.round(rng.standard_normal(V) * 2, 1)
+        T = float(rng.choice([0.5, 1.0, 1.7]))
+        k = int(rng.integers(1, V + 1))
+        p = float(rng.choice([0.3, 0.6, 0.9, 1.0]))
+        mp = float(rng.choice([0.05, 0.2, 0.5, 0.9]))
+        res = sample_row(x, row_params(V, T, k, p, mp), 0.3)
+        if res.cutoff_ambiguous:
+            continue
+        prob = np.exp((x - x.max()) / T)
+        prob /= prob.sum()
+        order = np.argsort(-x, kind="stable")
+        n_kp = sample_row(x, row_params(V, T, k, p), 0.3).kept
+        mask_kp = np.zeros(V, bool)
+        mask_kp[order[:n_kp]] = True
+        mask_min = prob >= prob.max() * mp
+        assert set(np.flatnonzero(res.r > 0)) == set(np.flatnonzero(mask_kp & mask_min))
+
+
+def test_min_p_logit_threshold_and_zero():
+    """p_i >= p_max * min_p  <=>  x_i >= m + T ln(min_p); min_p 0 changes
+    nothing."""
+    rng = np.random.default_rng(15)
+    for _ in range(50):
+        V = 3000
+        x = rng.standard_normal(V) * 3
+        T = float(rng.uniform(0.3, 2.0))
+        mp = float(rng.uniform(0.001, 0.9))
+        prob = np.exp((x - x.max()) / T)
+        q_sorted = np.sort(prob)[::-1] / prob.sum()
+        assert min_p_count(q_sorted, mp) == int(np.count_nonzero(x >= x.max() + T * np.log(mp)))
+        a = sample_row(x, row_params(V, T, 40, 0.9), 0.42)
+        b = sample_row(x, row_params(V, T, 40, 0.9, 0.0), 0.42)
+        assert a.kept == b.kept and a.token == b.token and np.array_equal(a.r, b.r)
+    assert row_params(10, 1.0, -1, 1.0, -0.5).min_p == 0.0
+    assert row_params(10, 1.0, -1, 1.0, float("nan")).min_p == 0.0
+    assert row_params(10, 1.0, -1, 1.0, 3.0).min_p == 1.0
 
 
 # --------------------------------------------------------- page table ---

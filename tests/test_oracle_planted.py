@@ -140,6 +140,21 @@ def _page_to_token_scaled(page_starts, page_size):
     return _real_page_to_token(np.asarray(page_starts) * page_size, page_size)
 
 
+def _min_p_strict(q_sorted, min_p):
+    # ">" for ">=": a token exactly at the threshold (or the maximum itself
+    # at min_p 1) is dropped
+    if min_p <= 0.0:
+        return len(q_sorted)
+    return int(np.count_nonzero(q_sorted > q_sorted[0] * min_p))
+
+
+def _min_p_absolute(q_sorted, min_p):
+    # threshold on the probability itself, not relative to the maximum
+    if min_p <= 0.0:
+        return len(q_sorted)
+    return max(1, int(np.count_nonzero(q_sorted >= min_p)))
+
+
 def _input_tuple_inclusive(table_idx, cached_len, device_len):
     # off by one: runs [cached_len, device_len]
     return _real_input_tuple(table_idx, cached_len, [int(d) + 1 for d in device_len])
@@ -175,6 +190,8 @@ PLANTS = [
     ("prepare", _prepare_k_strict, ["test_prepare_hand_worked_batch"]),
     ("prepare", _prepare_p_tensor_always, ["test_prepare_none_rules"]),
     ("paged_info", _paged_info_floor, ["test_paged_info_worked_count"]),
+    ("min_p_count", _min_p_strict, ["test_min_p_on_the_pages_logits"]),
+    ("min_p_count", _min_p_absolute, ["test_min_p_on_the_pages_logits"]),
     ("page_to_token", _page_to_token_scaled, ["test_page_aligned_allocation_pages_test"]),
 ]
 
@@ -183,7 +200,7 @@ PLANTS = [
 def test_planted_sampler_mistake_is_caught(monkeypatch, attr, bad, pin_names):
     monkeypatch.setattr(sr, attr, bad)
     for mod_name in ("filter_sorted", "inverse_cdf", "write_tokens", "gather_tokens",
-                     "input_tuple", "prepare", "paged_info", "page_to_token"):
+                     "input_tuple", "prepare", "paged_info", "page_to_token", "min_p_count"):
         if attr == mod_name:
             monkeypatch.setattr(pins, mod_name, bad)
     with pytest.raises(Exception):    # a failed assertion, or the oracle breaking outright

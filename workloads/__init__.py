@@ -61,6 +61,7 @@ class Workload:
     cols: np.ndarray                # [B] int64 (-1 => last column)
     seed: int = SAMPLER_SEED
     meta: dict = field(default_factory=dict)
+    min_p: Optional[np.ndarray] = None  # [B] float32 or None (disabled)
 
     @property
     def B(self) -> int:
@@ -303,3 +304,9 @@ def paged_batch(seed: int, n_req: int = 300, table_rows: int = 512, table_cols: 
     num_pages = (table_rows * table_cols) // page_size
     free_slots = rng.permutation(num_pages).astype(np.int64) * page_size
     return table_idx, cached_len, device_len, free_slots
+
+def with_min_p(w: Workload, values, seed: int = 0) -> Workload:
+    """The same batch with a per-request min_p drawn from ``values``."""
+    rng = np.random.default_rng([5000, seed])
+    mp = rng.choice(np.asarray(values, dtype=np.float32), w.B).astype(np.float32)
+    return replace(w, name=f"{w.name}+min_p", min_p=mp)
