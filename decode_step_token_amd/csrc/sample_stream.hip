@@ -643,15 +643,15 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         }
     };
 
-    // One tile ahead.  Candidate rows ask for their second tile only once the
-    // first has arrived: the theta selection below waits for the first tiles
-    // of all waves, which then come in sooner, and the second tiles stream
-    // in while it runs.
+    // One tile ahead.  Every row asks for its second tile only once the first
+    // has arrived: with the whole grid's first requests half as large, the
+    // first tiles come in sooner (the theta selection of candidate rows waits
+    // for the first tiles of all waves), and the second tiles stream in while
+    // the first are processed.
     uint4 raw[IO::U], nxt[IO::U];
     int t = wid;
     if (!use_row) {
         if (t < n_tiles) IO::load(row, V, t, lane, raw);
-        if (!want_cand && t + kWaves < n_tiles) IO::load(row, V, t + kWaves, lane, nxt);
     }
     if (threadIdx.x == 0) {
         ss.mbest = 0ull;
@@ -757,6 +757,18 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         }
     } else {
         lds_barrier();      // the merge slots above are set before any wave's merge
+        if (!use_row) {
+            // the second tile only once the first has arrived, as for
+            // candidate rows: a smaller first burst of requests from the
+            // whole grid brings every row's first tiles in sooner
+            float x0 = -INFINITY;
+            if (t < n_tiles) {
+#pragma unroll
+                for (int q = 0; q < Q; ++q) x0 = fmaxf(x0, IO::get(raw, q));
+            }
+            asm volatile("" :: "v"(x0) : "memory");
+            if (t + kWaves < n_tiles) IO::load(row, V, t + kWaves, lane, nxt);
+        }
     }
     if (!use_row) {
         if (t < n_tiles) process(raw, t);
