@@ -489,6 +489,14 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);  // wave-uniform
     const void* row = static_cast<const S*>(a.logits) + static_cast<int64_t>(b) * a.row_stride;
+    const int n_tiles = (V + IO::TILE - 1) / IO::TILE;
+    const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+    // The first tile is requested before anything waits on memory: its
+    // address does not depend on the row's parameters, whose (scalar) loads
+    // then overlap it.  Rows the re-reading path takes leave it unused.
+    uint4 raw[IO::U], nxt[IO::U];
+    int t = wid;
+    if (aligned && t < n_tiles) IO::load(row, V, t, lane, raw);
     const RowParams prm = row_params(a.temperature, a.top_k, a.top_p, a.min_p, b, V);
     // The Philox word is wave-uniform scalar work (ten 64-bit multiply rounds);
     // only wave 0 uses it, so only wave 0 pays for it on the CU's scalar unit.
@@ -499,7 +507,6 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         ss.minp = prm.min_p;
     }
     const double u = uniform24(word);       // valid in wave 0
-    const int n_tiles = (V + IO::TILE - 1) / IO::TILE;
 
     // min_p alone is a value cut on the same candidates as top-p: such rows
     // run as top-p rows (with p = 1)
@@ -508,7 +515,6 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     else if (prm.k < V) mode = kTopK;
     else if (prm.top_p || prm.min_p > 0.0f) mode = kTopP;
     else mode = kFull;
-    const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
     // rows one read cannot serve go straight to the re-reading path
     bool use_row = !aligned || (mode != kArgmax && n_tiles > kMaxTiles);
     const bool want_tiles = !use_row && mode == kFull;    // per-tile softmax sums
@@ -648,11 +654,6 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     // first tiles come in sooner (the theta selection of candidate rows waits
     // for the first tiles of all waves), and the second tiles stream in while
     // the first are processed.
-    uint4 raw[IO::U], nxt[IO::U];
-    int t = wid;
-    if (!use_row) {
-        if (t < n_tiles) IO::load(row, V, t, lane, raw);
-    }
     if (threadIdx.x == 0) {
         ss.mbest = 0ull;
         ss.mtotal = 0u;
