@@ -27,7 +27,7 @@
 //     edge of the histogram bin that holds the j-th largest of the 1024
 //     per-thread maxima.  j = k for top-k: j per-thread maxima are j distinct
 //     logits >= theta, so the top-k set is always inside the regions.  For
-//     top-p, j aims at about 1000 candidates.
+//     top-p, j aims at about 900 candidates.
 //
 // Finishing the row from the candidates is a sequence of block-wide passes
 // over the regions; after each one wave 0 reads what the pass produced and
@@ -53,7 +53,7 @@ constexpr int kCap = kWaves * kRegion;     // 8192
 constexpr int kMaxTiles = 512;
 constexpr int kList = 64;
 constexpr int kTopKCands = 4096;          // top-k rows: candidate count the threshold aims below
-constexpr int kTopPTarget = 1000;          // aimed-at candidate count for top-p rows
+constexpr int kTopPTarget = 900;           // aimed-at candidate count for top-p rows
 constexpr int kBins = 1024;                // candidate histograms: 16 bins per lane of wave 0
 constexpr int kBinsPerLane = kBins / kWave;
 constexpr int kTilesPerLane = kMaxTiles / kWave;
