@@ -1555,7 +1555,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             //   P (top-p without top-k): pick the bin where the descending weight
             //     reaches p * Z; list that bin while adding the weight of the
             //     bins above it per tile; rank the list, cut, add the kept part;
-            //     then the draw scans the per-tile weights block-wide.
+            //     then wave 0 draws from the per-tile weights.
             // Anything else (a boundary bin of more than kList entries, top-k
             // above kList with top-p) goes to the pass-driven descent below.
             const int sh_tile = kTileShift;
@@ -1666,43 +1666,35 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 if (lane == 0) ss.list_n = 0u;
                 wave_lds_sync();
             };
-            // block-wide draw from the per-tile kept weights (cleared here): the
-            // wave holding the first tile whose prefix exceeds u * W walks that
-            // tile's entries kept by ct in token order
-            auto block_tile_draw = [&](const Cut& ct) {
-                constexpr int TPW = kMaxTiles / kWaves;
-                const int tb = wid * TPW;
-                double v = 0.0;
-                if (lane < TPW) {
-                    v = ss.tacc[tb + lane];
-                    ss.tacc[tb + lane] = 0.0;
-                }
-                const double incl = wave_scan_f64_dpp(v);
-                if (lane == kWave - 1) ss.wtm[wid] = incl;
-                __syncthreads();
-                // every wave scans the 16 wave totals the same way (lane l holds
-                // wave l, tiles ascending)
-                const double tw = lane < kWaves ? ss.wtm[lane] : 0.0;
-                const double twi = wave_scan_f64_dpp(tw);
-                const double total_pre = readlane_f64(twi, kWaves - 1);
-                const double tgt = uniform24(ss.word) * total_pre;   // every wave
-                const uint64_t wb = __ballot(lane < kWaves && tw > 0.0 && twi > tgt);
-                const uint64_t nzw = __ballot(lane < kWaves && tw > 0.0);
-                const int cross = wb ? __ffsll(static_cast<unsigned long long>(wb)) - 1
-                                     : (nzw ? 63 - __clzll(static_cast<long long>(nzw)) : -1);
-                const double before = readlane_f64(twi - tw, wid);
-                if (wid == cross) {
-                    const double cum = before + incl;
-                    const uint64_t hb = __ballot(v > 0.0 && cum > tgt);
+            // wave 0: the draw from the per-tile kept weights, with W the kept
+            // mass the cut found: a scan over the tiles (64 at a time) finds
+            // the first tile whose prefix exceeds u * W, then a scan of that
+            // tile's entries kept by ct, in slot (token) order, the token
+            auto w0_tile_draw = [&](const Cut& ct, double W) {
+                const double tgt = u * W;
+                double run = 0.0, rem = INFINITY;
+                int ts = -1, last_t = -1;
+                for (int c0 = 0; c0 < n_tiles; c0 += kWave) {
+                    const int ti = c0 + lane;
+                    const double v = ti < n_tiles ? ss.tacc[ti] : 0.0;
+                    const double incl = wave_scan_f64_dpp(v);
                     const uint64_t nz = __ballot(v > 0.0);
-                    const int lx = hb ? __ffsll(static_cast<unsigned long long>(hb)) - 1
-                                      : 63 - __clzll(static_cast<long long>(nz));
-                    const double rem = hb ? tgt - readlane_f64(before + (incl - v), lx) : INFINITY;
-                    const int ts = tb + lx;
+                    if (nz) last_t = c0 + 63 - __clzll(static_cast<long long>(nz));
+                    const uint64_t hb = __ballot(v > 0.0 && run + incl > tgt);
+                    if (hb) {
+                        const int lx = __ffsll(static_cast<unsigned long long>(hb)) - 1;
+                        ts = c0 + lx;
+                        rem = tgt - (run + readlane_f64(incl - v, lx));
+                        break;
+                    }
+                    run += readlane_f64(incl, kWave - 1);
+                }
+                if (ts < 0) ts = last_t;        // rounding: u * W at or past the total
+                uint32_t found = 0xffffffffu, last = 0xffffffffu;
+                if (ts >= 0) {
                     const int sb = (ts & (kWaves - 1)) * kRegion + ss.tstart[ts];
                     const int n = ss.tcnt[ts];
                     double run2 = 0.0;
-                    uint32_t found = 0xffffffffu, last = 0xffffffffu;
                     for (int j0 = 0; j0 < n; j0 += kWave) {
                         const int j = j0 + lane;
                         double val = 0.0;
@@ -1722,12 +1714,11 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                         }
                         run2 += readlane_f64(in2, kWave - 1);
                     }
-                    if (lane == 0) {
-                        ss.res_token = found != 0xffffffffu ? found : last;
-                        ss.res_w = total_pre;
-                    }
                 }
-                __syncthreads();
+                if (lane == 0) {
+                    ss.res_token = found != 0xffffffffu ? found : (last != 0xffffffffu ? last : amax);
+                    ss.res_w = W;
+                }
             };
 
             // The histogram the routes pick from: the one each wave built after
@@ -1853,14 +1844,14 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                     const uint32_t ck = readlane_u32(in ? ss.skey[lane] : 0u, e);
                     const uint32_t cl = readlane_u32(in ? ss.sidx[lane] : 0u, e);
                     if (lane == 0) {
-                        ss.res_token = amax;      // replaced by the draw
                         ss.res_kept = bp.above_c + static_cast<uint32_t>(e) + 1u;
                         ss.cut_key = ck;
                         ss.cut_last = cl;
                     }
+                    wave_lds_sync();        // this wave's weights are in the tile sums
+                    w0_tile_draw(Cut{ck, cl}, bp.above_m + readlane_f64(incl, e));
                 }
                 __syncthreads();
-                block_tile_draw(Cut{ss.cut_key, ss.cut_last});
             }
             if (route == 1 || route == 2 || route == 4) {
                 fast = true;
