@@ -1935,7 +1935,6 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                     if (IO::index(tt, lane, q) < static_cast<uint32_t>(V)) {
                         float y;
                         const int d = depth_bin(IO::get(rb, q), &y);
-                        atomicAdd(&ss.hcnt[d], 1u);
                         atomicAdd(&ss.hmass[d], static_cast<double>(__builtin_amdgcn_exp2f(y)));
                     }
                 }
@@ -1943,6 +1942,13 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         }
         __syncthreads();
         if (wid == 0) {
+            // a bin is non-empty iff it holds weight: every bin above the
+            // deepest one has y > -64, so its entries weigh at least 2^-64; the
+            // deepest bin's entries may weigh nothing and can never be kept
+            // by a top-p cut (p < 1), so none is lost
+#pragma unroll
+            for (int i = 0; i < kBinsPerLane; ++i)
+                ss.hcnt[kBinsPerLane * lane + i] = ss.hmass[kBinsPerLane * lane + i] > 0.0 ? 1u : 0u;
             const BinPick bq = w0_pick_mass(ss.hcnt, ss.hmass, 0.0, ztgt / G);
             if (lane == 0) ss.bu[2] = static_cast<uint32_t>(bq.d < 0 ? 0 : bq.d);
         }
