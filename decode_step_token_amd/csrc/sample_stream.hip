@@ -1917,12 +1917,19 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             const int bq = dq < 1.0f ? 0 : (dq >= static_cast<float>(kBins - 1) ? kBins - 1 : static_cast<int>(dq));
             return kBins - 1 - bq;
         };
-        ss.hcnt[threadIdx.x] = 0u;
-        ss.hmass[threadIdx.x] = 0.0;
+        // pass A's histogram: kHistCopies adjacent copies of each bin, lane l
+        // adding to copy l mod kHistCopies (so lanes of a wave seldom meet on one
+        // address), kept in the candidate regions, which pass B refills
+        constexpr int kHistCopies = 8;
+        static_assert(sizeof(double) * kBins * kHistCopies <= sizeof(ss.cent), "histogram copies fit");
+        double* const hist = reinterpret_cast<double*>(ss.cent);
+#pragma unroll
+        for (int c = 0; c < kHistCopies; ++c) hist[threadIdx.x * kHistCopies + c] = 0.0;
         if (threadIdx.x == 0) { ss.movf = 0u; ss.mtotal = 0u; }
         __syncthreads();
         // (A)
         {
+            double* const hl = hist + (lane & (kHistCopies - 1));
             uint4 ra[IO::U], rb[IO::U];
             int tt = wid;
             if (tt < n_tiles) IO::load(row, V, tt, lane, ra);
@@ -1935,10 +1942,17 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                     if (IO::index(tt, lane, q) < static_cast<uint32_t>(V)) {
                         float y;
                         const int d = depth_bin(IO::get(rb, q), &y);
-                        atomicAdd(&ss.hmass[d], static_cast<double>(__builtin_amdgcn_exp2f(y)));
+                        atomicAdd(&hl[d * kHistCopies], static_cast<double>(__builtin_amdgcn_exp2f(y)));
                     }
                 }
             }
+        }
+        __syncthreads();
+        {
+            double hs = 0.0;
+#pragma unroll
+            for (int c2 = 0; c2 < kHistCopies; ++c2) hs += hist[threadIdx.x * kHistCopies + c2];
+            ss.hmass[threadIdx.x] = hs;
         }
         __syncthreads();
         if (wid == 0) {
