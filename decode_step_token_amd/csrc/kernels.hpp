@@ -32,6 +32,7 @@ struct SampleArgs {
     const float* min_p;        // may be null
     const int64_t* uid;        // non-null unless temperature is null
     uint64_t step, seed;
+    int resident;              // stream blocks resident at once (0: unknown)
     int32_t* tokens_out;
     float* probs_out;
     int32_t* kept_out;

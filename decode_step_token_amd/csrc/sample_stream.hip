@@ -475,6 +475,47 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// --------------------------------------------------------------- row order --
+// Sampled rows with top-k off and top-p or min_p on may take the flat-row or
+// the re-reading path, several times longer than a stream.  One block of this
+// kernel fills a compute unit (its LDS and registers), so a grid of more rows
+// than compute units runs in rounds, blocks starting in index order as units
+// free up.  Block g then takes the g-th row of the order "those long rows
+// first, then the rest" (each part in index order): the long rows start in
+// the first round instead of lengthening the last.  Every wave finds the same
+// row by itself.
+
+__device__ __forceinline__ bool long_row(const SampleArgs& a, int r) {
+    const RowParams p = row_params(a.temperature, a.top_k, a.top_p, a.min_p, r, a.V);
+    return !p.greedy && p.k == a.V && (p.top_p || p.min_p > 0.0f);
+}
+
+__device__ int long_rows_first(const SampleArgs& a, int g) {
+    const int lane = threadIdx.x & (kWave - 1);
+    // the long rows' count: rows i*64 + lane, one coalesced read per parameter
+    uint32_t n_long = 0;
+#pragma unroll 4
+    for (int r0 = 0; r0 < a.B; r0 += kWave) {
+        const int r = r0 + lane;
+        n_long += static_cast<uint32_t>(__popcll(__ballot(r < a.B && long_row(a, r))));
+    }
+    const bool want_long = static_cast<uint32_t>(g) < n_long;
+    uint32_t left = want_long ? static_cast<uint32_t>(g) : static_cast<uint32_t>(g) - n_long;
+    // the left-th (from 0) row of the wanted kind, 64 rows at a time
+    for (int r0 = 0; r0 < a.B; r0 += kWave) {
+        const int r = r0 + lane;
+        const uint64_t m = __ballot(r < a.B && long_row(a, r) == want_long);
+        const uint32_t c = static_cast<uint32_t>(__popcll(m));
+        if (left < c) {
+            const uint64_t below = lane ? (m & (~0ull >> (kWave - lane))) : 0ull;
+            const uint64_t hit = __ballot(((m >> lane) & 1ull) && static_cast<uint32_t>(__popcll(below)) == left);
+            return r0 + __ffsll(static_cast<unsigned long long>(hit)) - 1;
+        }
+        left -= c;
+    }
+    return g;    // not reached: the wanted part holds more than left rows
+}
+
 // ------------------------------------------------------------------ kernel --
 
 template <int DT>
@@ -484,7 +525,8 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     constexpr int Q = IO::Q;
     __shared__ Smem ss;
 
-    const int b = blockIdx.x;
+    const int b = a.resident > 0 && a.B > a.resident && a.temperature != nullptr
+        ? long_rows_first(a, static_cast<int>(blockIdx.x)) : static_cast<int>(blockIdx.x);
     const int V = a.V;
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);  // wave-uniform

@@ -56,6 +56,7 @@ struct dst_sampler {
     int vocab = 0;
     int dtype = 0;
     uint64_t seed = 0;
+    int cus = 0;                       // compute units: stream blocks resident at once
     void* workspace = nullptr;       // device: argmax slots and counters
     uint64_t* slot = nullptr;
     uint32_t* count = nullptr;
@@ -148,6 +149,10 @@ int sampler_create(dst_sampler** out, int device, int32_t max_batch, int32_t voc
     s->dtype = logits_dtype;
     s->seed = seed;
     DeviceGuard g(device);
+    if (hipDeviceGetAttribute(&s->cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
+        (void)hipGetLastError();
+        s->cus = 0;                    // unknown: rows keep their index order
+    }
 
     const size_t slot_bytes = sizeof(uint64_t) * static_cast<size_t>(max_batch);
     const size_t count_bytes = sizeof(uint32_t) * static_cast<size_t>(max_batch);
@@ -237,6 +242,7 @@ int sample_batch(dst_sampler* s, void* stream, const void* logits, int64_t row_s
         a.uid = uid;
         a.step = step;
         a.seed = s->seed;
+        a.resident = s->cus;
         a.tokens_out = tokens_out;
         if (dbg) {
             a.probs_out = dbg->probs_out;
