@@ -483,7 +483,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 // free up.  Block g then takes the g-th row of the order "those long rows
 // first, then the rest" (each part in index order): the long rows start in
 // the first round instead of lengthening the last.  Every wave finds the same
-// row by itself.
+// row by itself, from one read of the parameters; larger batches keep index
+// order.
+
+constexpr int kOrderChunks = 8;     // batches of up to 8 * 64 rows are reordered
 
 __device__ __forceinline__ bool long_row(const SampleArgs& a, int r) {
     const RowParams p = row_params(a.temperature, a.top_k, a.top_p, a.min_p, r, a.V);
@@ -492,28 +495,38 @@ __device__ __forceinline__ bool long_row(const SampleArgs& a, int r) {
 
 __device__ int long_rows_first(const SampleArgs& a, int g) {
     const int lane = threadIdx.x & (kWave - 1);
-    // the long rows' count: rows i*64 + lane, one coalesced read per parameter
+    // one coalesced read per parameter and 64 rows (rows past B read row
+    // B - 1 and are masked off), the long-row masks kept per 64 rows
+    uint64_t m[kOrderChunks];
     uint32_t n_long = 0;
-#pragma unroll 4
-    for (int r0 = 0; r0 < a.B; r0 += kWave) {
-        const int r = r0 + lane;
-        n_long += static_cast<uint32_t>(__popcll(__ballot(r < a.B && long_row(a, r))));
+#pragma unroll
+    for (int c = 0; c < kOrderChunks; ++c) {
+        const int r = c * kWave + lane;
+        const bool lr = long_row(a, r < a.B ? r : a.B - 1);
+        m[c] = __ballot(r < a.B && lr);
+        n_long += static_cast<uint32_t>(__popcll(m[c]));
     }
     const bool want_long = static_cast<uint32_t>(g) < n_long;
     uint32_t left = want_long ? static_cast<uint32_t>(g) : static_cast<uint32_t>(g) - n_long;
-    // the left-th (from 0) row of the wanted kind, 64 rows at a time
-    for (int r0 = 0; r0 < a.B; r0 += kWave) {
-        const int r = r0 + lane;
-        const uint64_t m = __ballot(r < a.B && long_row(a, r) == want_long);
-        const uint32_t c = static_cast<uint32_t>(__popcll(m));
-        if (left < c) {
-            const uint64_t below = lane ? (m & (~0ull >> (kWave - lane))) : 0ull;
-            const uint64_t hit = __ballot(((m >> lane) & 1ull) && static_cast<uint32_t>(__popcll(below)) == left);
-            return r0 + __ffsll(static_cast<unsigned long long>(hit)) - 1;
+    // the 64 rows holding the wanted one, and its rank among them
+    uint64_t sm = 0ull;
+    int sr0 = -1;
+#pragma unroll
+    for (int c = 0; c < kOrderChunks; ++c) {
+        const int r0 = c * kWave;
+        const int nv = a.B - r0;
+        const uint64_t valid = nv <= 0 ? 0ull : (nv >= kWave ? ~0ull : (1ull << nv) - 1ull);
+        const uint64_t mc = want_long ? m[c] : (~m[c] & valid);
+        const uint32_t cnt = static_cast<uint32_t>(__popcll(mc));
+        if (sr0 < 0) {
+            if (left < cnt) { sm = mc; sr0 = r0; }
+            else left -= cnt;
         }
-        left -= c;
     }
-    return g;    // not reached: the wanted part holds more than left rows
+    if (sr0 < 0) return g;    // not reached: the wanted part holds more than left rows
+    const uint64_t below = lane ? (sm & (~0ull >> (kWave - lane))) : 0ull;
+    const uint64_t hit = __ballot(((sm >> lane) & 1ull) && static_cast<uint32_t>(__popcll(below)) == left);
+    return sr0 + __ffsll(static_cast<unsigned long long>(hit)) - 1;
 }
 
 // ------------------------------------------------------------------ kernel --
@@ -525,7 +538,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     constexpr int Q = IO::Q;
     __shared__ Smem ss;
 
-    const int b = a.resident > 0 && a.B > a.resident && a.temperature != nullptr
+    const int b = a.resident > 0 && a.B > a.resident && a.B <= kOrderChunks * kWave && a.temperature != nullptr
         ? long_rows_first(a, static_cast<int>(blockIdx.x)) : static_cast<int>(blockIdx.x);
     const int V = a.V;
     const int lane = threadIdx.x & (kWave - 1);

@@ -74,11 +74,13 @@ def test_min_p_zero_changes_nothing():
     assert np.array_equal(a["tokens"], b["tokens"])
 
 
-@pytest.mark.parametrize("B,V,dtype,seed", [(777, 2000, "bf16", 11), (1500, 700, "f32", 12)])
+@pytest.mark.parametrize("B,V,dtype,seed", [(500, 2000, "bf16", 11), (512, 3000, "f32", 13),
+                                          (777, 1000, "bf16", 14), (1500, 700, "f32", 12)])
 def test_more_rows_than_compute_units(B, V, dtype, seed):
-    """More rows than blocks resident at once: the long rows (sampled, top-k
-    off, top-p or min_p on) are started first; every row still lands in its
-    own outputs, checked on every row against the oracle."""
+    """More rows than blocks resident at once: up to 512 rows the long rows
+    (sampled, top-k off, top-p or min_p on) are started first, larger batches
+    keep index order; every row still lands in its own outputs, checked on
+    every row against the oracle."""
     rng = np.random.default_rng(seed)
     w = wl.with_min_p(wl.tiny(rng, B, V, dtype), [0.0, 0.0, 0.0, 0.05, 0.3], seed)
     _check(w)
