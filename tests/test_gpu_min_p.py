@@ -84,3 +84,26 @@ def test_more_rows_than_compute_units(B, V, dtype, seed):
     rng = np.random.default_rng(seed)
     w = wl.with_min_p(wl.tiny(rng, B, V, dtype), [0.0, 0.0, 0.0, 0.05, 0.3], seed)
     _check(w)
+
+
+@pytest.mark.parametrize("case", ["scattered", "all_long", "none_long"])
+def test_long_rows_first_edges(case):
+    """Reordered batches (257 <= B <= 512) with the long rows at the very end
+    and scattered, with every row long, and with none: each row's token
+    still equals the oracle's."""
+    B, V = 300, 1500
+    rng = np.random.default_rng({"scattered": 21, "all_long": 22, "none_long": 23}[case])
+    w = wl.tiny(rng, B, V, "f32")
+    T = np.full(B, 0.8, np.float32)
+    k = np.full(B, 20, np.int64)
+    p = np.full(B, 0.9, np.float64)
+    if case == "scattered":
+        T[::7] = 0.0                               # greedy rows are never long
+        for r in (B - 1, 150, 3, 0):
+            T[r], k[r], p[r] = 1.1, -1, 0.85       # top-p without top-k
+    elif case == "all_long":
+        k[:] = -1
+    w.temperature[:] = T
+    w.top_k[:] = k.astype(w.top_k.dtype)
+    w.top_p[:] = p.astype(w.top_p.dtype)
+    _check(w)
