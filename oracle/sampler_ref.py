@@ -38,7 +38,12 @@ design notes):
 
 Ambiguity flags (decisions that rounding order may legitimately flip):
 ``draw_ambiguous`` when ``u`` lies within 1e-5 of a CDF boundary, and
-``cutoff_ambiguous`` when an exclusive prefix lies within 1e-6 of top_p.
+``cutoff_ambiguous`` when a comparison that sets the kept length could be
+flipped by rounding: an exclusive prefix after the first rank within 1e-6 of
+top_p (the first rank's prefix is exactly 0 and is always kept), or a token
+within 1e-9 of the min_p threshold in log-probability.  The alternative kept
+lengths are exactly the ones those flips can give (``cutoff_alternatives``,
+``min_p_alternatives``).
 """
 from __future__ import annotations
 
@@ -180,12 +185,49 @@ def _distribution(x: np.ndarray, T: float, pi: np.ndarray, n: int) -> np.ndarray
 
 
 def _acceptable(r: np.ndarray, u: float):
+    """(near, tokens): whether ``u`` lies within DRAW_BAND of a CDF boundary
+    of a kept token, and the kept tokens whose interval [C_{i-1}, C_i),
+    widened by DRAW_BAND on both sides, contains ``u``."""
     c = np.cumsum(r)
     prev = np.concatenate(([0.0], c[:-1]))
     kept = r > 0
     ok = np.flatnonzero(kept & (prev - DRAW_BAND <= u) & (u < c + DRAW_BAND))
     near = np.abs(np.concatenate((prev[kept], c[kept])) - u).min() < DRAW_BAND
     return bool(near), [int(i) for i in ok]
+
+
+def cutoff_alternatives(q_sorted: np.ndarray, k: int, p: float) -> set:
+    """Kept lengths of the top-k-then-top-p filter that rounding of the
+    exclusive prefixes may also give.  Rank j is kept iff S_j < p; S_0 = 0 is
+    exact (the first rank is always kept), and every later S_j is a sum that
+    rounding may move by up to CUT_BAND.  Since S_j never decreases along the
+    order, the reachable lengths are every count between the one at
+    p - CUT_BAND and the one at p + CUT_BAND ("The engine and the sampler",
+    section "The sampler": the top-p test on the renormalised top-k masses).
+    Returns the set of lengths (the exact one included)."""
+    k = min(k, len(q_sorted))
+    if p >= 1.0:
+        return {k}
+    q = q_sorted[:k] / q_sorted[:k].sum()
+    before = np.cumsum(q)[:-1]          # S_1 .. S_{k-1}
+    n_lo = 1 + int(np.count_nonzero(before < p - CUT_BAND))
+    n_hi = 1 + int(np.count_nonzero(before < p + CUT_BAND))
+    return set(range(n_lo, n_hi + 1))
+
+
+def min_p_alternatives(x_sorted: np.ndarray, T: float, min_p: float) -> set:
+    """Kept lengths of the min_p filter that rounding may also give: rank j
+    is kept iff d_j = (x_j - x_0)/T - ln(min_p) >= 0 (the probability at least
+    min_p times the largest); a d_j within MIN_P_BAND of 0 may go either way.
+    d never increases along the order, so the reachable lengths run from
+    #{d >= MIN_P_BAND} to #{d > -MIN_P_BAND}.  Returns the set of lengths
+    (the exact one included); empty when min_p is off."""
+    if min_p <= 0.0:
+        return set()
+    d = (x_sorted - x_sorted[0]) / T - np.log(min_p)
+    lo = int(np.count_nonzero(d >= MIN_P_BAND))
+    hi = int(np.count_nonzero(d > -MIN_P_BAND))
+    return set(range(lo, hi + 1))
 
 
 def sample_row(x: np.ndarray, params: RowParams, u: float, word0: int = 0,
@@ -214,21 +256,8 @@ def sample_row(x: np.ndarray, params: RowParams, u: float, word0: int = 0,
     if not want_alternatives:
         return res
     # kept lengths that rounding at a cut-off may also give
-    kp_alts = {n_kp}
-    if order == "k_then_p" and params.p < 1.0:
-        k = min(params.k, V)
-        q = q_sorted[:k] / q_sorted[:k].sum()
-        before = np.concatenate(([0.0], np.cumsum(q)[:-1]))
-        if np.any(np.abs(before - params.p) < CUT_BAND):
-            kp_alts |= {a for a in (n_kp - 1, n_kp + 1) if 1 <= a <= k}
-    min_alts = {n_min}
-    if params.min_p > 0.0:
-        # distance to the min_p threshold in log-probability
-        d = (x[pi] - m) / params.T - np.log(params.min_p)
-        near = np.abs(d) < MIN_P_BAND
-        if np.any(near):
-            min_alts |= {int(np.count_nonzero(d > MIN_P_BAND)),
-                         int(np.count_nonzero(d >= -MIN_P_BAND))}
+    kp_alts = cutoff_alternatives(q_sorted, params.k, params.p) if order == "k_then_p" else {n_kp}
+    min_alts = min_p_alternatives(x[pi], params.T, params.min_p) or {n_min}
     alts = {min(a, b) for a in kp_alts for b in min_alts} - {n}
     alts = {a for a in alts if a >= 1}
     if alts:

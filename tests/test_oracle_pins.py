@@ -16,6 +16,7 @@ import scipy.special
 import scipy.stats
 
 import oracle
+import oracle.sampler_ref as sr
 from oracle import (filter_sorted, inverse_cdf, philox4x64, request_uniform, request_word,
                     row_params, sample_batch, sample_row, widen_logits, write_tokens)
 from oracle import (PagePool, gather_tokens, input_tuple, min_p_count, page_to_token, paged_info,
@@ -581,6 +582,65 @@ def test_page_table_brute_force():
                     touched[t, page * ps + o] = True
                 k += 1
         assert k == needed and np.array_equal(table[~touched], table0[~touched])
+
+
+def test_draw_band_accepts_exactly_the_near_tokens():
+    """The draw's tolerance: with dyadic masses the CDF boundaries are exact
+    (0.25, 0.5, 1), so which tokens a u near a boundary may give is known by
+    hand: both neighbours within 1e-5 of the boundary, only the owner beyond,
+    never a token of zero mass ("The engine and the sampler", section "The
+    sampler": one categorical draw from the kept distribution)."""
+    r = np.array([0.25, 0.0, 0.25, 0.5])
+    cases = [
+        (0.5 - 0.5e-5, True, [2, 3]),
+        (0.5 - 2e-5, False, [2]),
+        (0.5 + 0.5e-5, True, [2, 3]),
+        (0.5 + 2e-5, False, [3]),
+        (0.25 + 0.5e-5, True, [0, 2]),
+        (0.25 - 2e-5, False, [0]),
+        (0.75, False, [3]),
+    ]
+    for u, near, toks in cases:
+        got_near, got = sr._acceptable(r, u)
+        assert got_near == near and got == toks, (u, got_near, got)
+        assert sr.inverse_cdf(r, u) in got
+
+
+def test_cutoff_band_hand_worked():
+    """Which kept lengths rounding of the top-p prefixes may give.  With
+    masses (1/2, 1/4, 1/8, 1/8) the exclusive prefixes 0, 0.5, 0.75, 0.875
+    are exact, so a p within 1e-6 of 0.75 may keep 2 or 3 and a p 5e-6 away
+    keeps exactly one of them.  The first prefix is exactly 0: at the
+    clamped top_p = float32(1e-6) only the first token is kept, with no
+    alternative ("The engine and the sampler", section "The sampler": the
+    most likely token always stays)."""
+    q = np.array([0.5, 0.25, 0.125, 0.125])
+    assert sr.cutoff_alternatives(q, 4, 0.75 - 5e-7) == {2, 3}
+    assert sr.cutoff_alternatives(q, 4, 0.75 + 5e-7) == {2, 3}
+    assert sr.cutoff_alternatives(q, 4, 0.75 - 5e-6) == {2}
+    assert sr.cutoff_alternatives(q, 4, 0.75 + 5e-6) == {3}
+    assert sr.cutoff_alternatives(q, 4, float(np.float32(1e-6))) == {1}
+    assert sr.cutoff_alternatives(q, 4, 1.0) == {4}
+    # top-k 2 renormalises first: (2/3, 1/3), prefixes 0, 2/3
+    assert sr.cutoff_alternatives(q, 2, 2.0 / 3.0 + 5e-7) == {1, 2}
+    assert sr.cutoff_alternatives(q, 2, 0.7) == {2}
+    res = sr.sample_row(np.array([3.0, 1.0, 0.5, 0.2, 0.1, 0.0]), sr.row_params(6, 1.0, -1, 1e-9), 0.3)
+    assert res.kept == 1 and not res.cutoff_ambiguous and res.token == 0
+
+
+def test_min_p_band_hand_worked():
+    """The min_p threshold's tolerance: a token 1e-10 from the threshold in
+    log-probability may go either way, one 1e-8 away may not ("The engine and
+    the sampler", section "Exercises", exercise 2: p_i >= min_p * p_max)."""
+    prm = sr.row_params(5, 1.0, -1, 1.0, min_p=0.5)
+    thr = float(np.log(prm.min_p))
+    for off, want in [(1e-10, {1, 2}), (-1e-10, {1, 2}), (1e-8, {2}), (-1e-8, {1})]:
+        x = np.array([0.0, thr + off, -5.0, -6.0, -7.0])
+        assert sr.min_p_alternatives(x, prm.T, prm.min_p) == want, off
+        res = sr.sample_row(x, prm, 0.3)
+        assert res.kept == (2 if off > 0 else 1)
+        assert res.cutoff_ambiguous == (abs(off) < 1e-9)
+    assert sr.min_p_alternatives(np.array([0.0, -1.0]), 1.0, 0.0) == set()
 
 
 def test_module_header_marks_test_infrastructure():

@@ -160,6 +160,65 @@ def _input_tuple_inclusive(table_idx, cached_len, device_len):
     return _real_input_tuple(table_idx, cached_len, [int(d) + 1 for d in device_len])
 
 
+def _acceptable_wide(r, u):
+    # the draw band ten times too wide
+    c = np.cumsum(r)
+    prev = np.concatenate(([0.0], c[:-1]))
+    kept = r > 0
+    band = 1e-4
+    ok = np.flatnonzero(kept & (prev - band <= u) & (u < c + band))
+    near = np.abs(np.concatenate((prev[kept], c[kept])) - u).min() < band
+    return bool(near), [int(i) for i in ok]
+
+
+def _acceptable_zero_mass(r, u):
+    # tokens of zero mass accepted next to a boundary
+    c = np.cumsum(r)
+    prev = np.concatenate(([0.0], c[:-1]))
+    band = sr.DRAW_BAND
+    ok = np.flatnonzero((prev - band <= u) & (u < c + band))
+    near = np.abs(np.concatenate((prev, c)) - u).min() < band
+    return bool(near), [int(i) for i in ok]
+
+
+def _cutoff_band_includes_first(q_sorted, k, p):
+    # the exact S_0 = 0 treated as if rounding could move it
+    k = min(k, len(q_sorted))
+    if p >= 1.0:
+        return {k}
+    q = q_sorted[:k] / q_sorted[:k].sum()
+    before = np.concatenate(([0.0], np.cumsum(q)[:-1]))
+    n = int(np.count_nonzero(before < p))
+    out = {n}
+    if np.any(np.abs(before - p) < sr.CUT_BAND):
+        out |= {a for a in (n - 1, n + 1) if 1 <= a <= k}
+    return out
+
+
+_real_cutoff_alternatives = sr.cutoff_alternatives
+
+
+def _cutoff_band_wide(q_sorted, k, p):
+    old = sr.CUT_BAND
+    sr.CUT_BAND = 1e-5
+    try:
+        return _real_cutoff_alternatives(q_sorted, k, p)
+    finally:
+        sr.CUT_BAND = old
+
+
+_real_min_p_alternatives = sr.min_p_alternatives
+
+
+def _min_p_band_wide(x_sorted, T, min_p):
+    old = sr.MIN_P_BAND
+    sr.MIN_P_BAND = 1e-7
+    try:
+        return _real_min_p_alternatives(x_sorted, T, min_p)
+    finally:
+        sr.MIN_P_BAND = old
+
+
 def _run_pins(names):
     for name in names:
         fn = getattr(pins, name)
@@ -193,6 +252,11 @@ PLANTS = [
     ("min_p_count", _min_p_strict, ["test_min_p_on_the_pages_logits"]),
     ("min_p_count", _min_p_absolute, ["test_min_p_on_the_pages_logits"]),
     ("page_to_token", _page_to_token_scaled, ["test_page_aligned_allocation_pages_test"]),
+    ("_acceptable", _acceptable_wide, ["test_draw_band_accepts_exactly_the_near_tokens"]),
+    ("_acceptable", _acceptable_zero_mass, ["test_draw_band_accepts_exactly_the_near_tokens"]),
+    ("cutoff_alternatives", _cutoff_band_includes_first, ["test_cutoff_band_hand_worked"]),
+    ("cutoff_alternatives", _cutoff_band_wide, ["test_cutoff_band_hand_worked"]),
+    ("min_p_alternatives", _min_p_band_wide, ["test_min_p_band_hand_worked"]),
 ]
 
 
