@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdst_sampler.so")
 
-SOURCES = ["argmax.hip", "sample_exact.hip", "sample_stream.hip", "write_tokens.hip",
+SOURCES = ["sample_split.hip", "sample_exact.hip", "write_tokens.hip",
            "prepare.hip", "page_table.hip", "sampler_api.hip"]
 HEADERS = ["device_common.hpp", "kernels.hpp", "exact_path.hpp"]
 

@@ -99,7 +99,7 @@ __device__ __forceinline__ int tile_slice(const void* row, int V, int64_t base, 
 // key, and through *rem how many elements equal to it are taken and through
 // *eq how many equal elements satisfy pred.
 template <int DT, int BLOCK, typename P>
-__device__ uint32_t exact_select_kth(const void* row, int V, uint32_t r, P pred, ExactSmem& sm,
+__device__ __forceinline__ uint32_t exact_select_kth(const void* row, int V, uint32_t r, P pred, ExactSmem& sm,
                                      uint32_t* rem, uint32_t* eq) {
     uint32_t prefix = 0, mask = 0;
     for (int shift = 24; shift >= 0; shift -= 8) {
@@ -134,7 +134,7 @@ __device__ uint32_t exact_select_kth(const void* row, int V, uint32_t r, P pred,
 // Index of the n-th (1-based) element in token order with key == key and
 // pred(i, key).  Returns -1 if there are fewer.
 template <int DT, int BLOCK, typename P>
-__device__ int64_t exact_nth_equal(const void* row, int V, uint32_t key, uint32_t n, P pred,
+__device__ __forceinline__ int64_t exact_nth_equal(const void* row, int V, uint32_t key, uint32_t n, P pred,
                                    ExactSmem& sm) {
     constexpr int VEC = Elem<DT>::kVec;
     constexpr int64_t TILE = static_cast<int64_t>(BLOCK) * VEC;
@@ -170,7 +170,7 @@ __device__ int64_t exact_nth_equal(const void* row, int V, uint32_t key, uint32_
 
 // Cut holding the r-th largest element (1-based) and everything above it.
 template <int DT, int BLOCK, typename P>
-__device__ Cut exact_cut_by_count(const void* row, int V, uint32_t r, P pred, ExactSmem& sm) {
+__device__ __forceinline__ Cut exact_cut_by_count(const void* row, int V, uint32_t r, P pred, ExactSmem& sm) {
     uint32_t rem, eq;
     const uint32_t key = exact_select_kth<DT, BLOCK>(row, V, r, pred, sm, &rem, &eq);
     Cut c{key, INT64_MAX};
@@ -182,7 +182,7 @@ __device__ Cut exact_cut_by_count(const void* row, int V, uint32_t r, P pred, Ex
 // exclusive prefix mass reaches `target` ends at the returned cut.  Returns
 // `base` itself if the mass never reaches it (rounding only).
 template <int DT, int BLOCK>
-__device__ Cut exact_cut_by_mass(const void* row, int V, const Cut& base, double target, float m,
+__device__ __forceinline__ Cut exact_cut_by_mass(const void* row, int V, const Cut& base, double target, float m,
                                  float T, ExactSmem& sm) {
     uint32_t prefix = 0, mask = 0;
     double above = 0.0;
@@ -247,7 +247,7 @@ __device__ Cut exact_cut_by_mass(const void* row, int V, const Cut& base, double
 
 // First n (<= 64) indices of the descending order into out[0..63], -1 padded.
 template <int DT, int BLOCK>
-__device__ void exact_debug_topk(const void* row, int V, int n, int32_t* out, ExactSmem& sm) {
+__device__ __forceinline__ void exact_debug_topk(const void* row, int V, int n, int32_t* out, ExactSmem& sm) {
     const Cut c = exact_cut_by_count<DT, BLOCK>(row, V, static_cast<uint32_t>(n),
                                                  [](int64_t, uint32_t) { return true; }, sm);
     if (threadIdx.x == 0) sm.list_n = 0;
@@ -282,7 +282,7 @@ __device__ void exact_debug_topk(const void* row, int V, int n, int32_t* out, Ex
 // Debug outputs common to every path once the kept cut is known: the final
 // distribution (one more pass) and the descending-order index list.
 template <int DT, int BLOCK>
-__device__ __noinline__ void exact_debug_outputs(const SampleArgs& a, int b, const void* row,
+__device__ __forceinline__ void exact_debug_outputs(const SampleArgs& a, int b, const void* row,
                                     const RowParams& prm, const Cut& cut, float m, double W,
                                     ExactSmem& sm) {
     const int V = a.V;
@@ -303,7 +303,7 @@ __device__ __noinline__ void exact_debug_outputs(const SampleArgs& a, int b, con
 
 // Argmax row: token, and the debug outputs of a one-hot distribution.
 template <int BLOCK>
-__device__ void finish_argmax_row(const SampleArgs& a, int b, int32_t amax, uint64_t word) {
+__device__ __forceinline__ void finish_argmax_row(const SampleArgs& a, int b, int32_t amax, uint64_t word) {
     if (threadIdx.x == 0) {
         a.tokens_out[b] = amax;
         if (a.kept_out) a.kept_out[b] = 1;
@@ -319,10 +319,10 @@ __device__ void finish_argmax_row(const SampleArgs& a, int b, int32_t amax, uint
     }
 }
 
-// The whole row by the exact multi-pass algorithm.  Kept out of line: it is
-// the rare path, and inlining it would crowd the callers' registers.
+// The whole row by the exact multi-pass algorithm.  Inline like everything
+// else: a call would give the calling kernel a scratch stack.
 template <int DT, int BLOCK>
-__device__ __noinline__ void exact_row(const SampleArgs& a, int b, const void* row, const RowParams& prm,
+__device__ __forceinline__ void exact_row(const SampleArgs& a, int b, const void* row, const RowParams& prm,
                           uint64_t word, double u, ExactSmem& sm) {
     constexpr int VEC = Elem<DT>::kVec;
     constexpr int64_t TILE = static_cast<int64_t>(BLOCK) * VEC;

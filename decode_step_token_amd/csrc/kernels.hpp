@@ -22,6 +22,26 @@ struct ArgmaxArgs {
     uint64_t* rand_out;
 };
 
+// Split-row sampler: per (row, chunk) record published by the chunk's
+// workgroup and read by the row's finishing workgroup (128 bytes).
+struct SplitRec {
+    float m;           // chunk maximum
+    uint32_t amax;     // lowest index holding it (argmax rows)
+    float theta;       // every chunk element >= theta is among the candidates
+    uint32_t cnt;      // candidates published; kSplitCap + 1: too many, none published
+    double z;          // sum of the chunk's weights 2^(x c - rc)
+    float rc;          // fl(m * c): the weights' reference
+    uint32_t mode;
+    float seg[16];     // weight sums of the chunk's 16-byte-load slots
+    uint32_t pad[8];
+};
+static_assert(sizeof(SplitRec) == 128, "record size");
+
+constexpr int kSplitThreads = 256;
+constexpr int kSplitCap = 256;        // candidates one chunk may publish
+constexpr int kSplitMaxChunks = 64;   // chunks per row (one flag per lane of a wave)
+constexpr int kSplitXcds = 8;         // rows are dealt to the XCDs round robin
+
 struct SampleArgs {
     const void* logits;
     int64_t row_stride;
@@ -38,6 +58,13 @@ struct SampleArgs {
     int32_t* kept_out;
     int32_t* topk_idx_out;
     uint64_t* rand_out;
+    // split-row sampler workspace (see SplitRec)
+    SplitRec* rec;             // [B][rec_stride]
+    uint64_t* cand;            // [B][rec_stride][kSplitCap] (order key << 32 | index)
+    uint32_t* flags;           // [B][kSplitMaxChunks] epoch of the last publication
+    int rec_stride;            // chunks allocated per row
+    int chunks;                // chunks per row in this launch
+    uint32_t epoch;            // nonzero, different for every launch on a workspace
 };
 
 struct WriteArgs {
@@ -74,6 +101,12 @@ hipError_t launch_argmax(const ArgmaxArgs& args, int dtype, hipStream_t stream);
 void argmax_plan(int B, int V, int dtype, int* chunks, int* chunk_len);
 hipError_t launch_sample_exact(const SampleArgs& args, int dtype, hipStream_t stream);
 hipError_t launch_sample_stream(const SampleArgs& args, int dtype, hipStream_t stream);
+// loads per thread and chunk for the split-row sampler (4, 8 or 16), 0 if V needs more
+// than kSplitMaxChunks chunks even at 16; *chunks receives the chunk count
+int split_plan(int V, int dtype, int* chunks);
+// chunks per row the workspace must hold for a vocabulary (0: the split sampler is not used)
+int split_chunks_alloc(int V, int dtype);
+hipError_t launch_sample_split(const SampleArgs& args, int dtype, int nl, hipStream_t stream);
 hipError_t launch_write_tokens(const WriteArgs& args, hipStream_t stream);
 hipError_t launch_gather_tokens(const GatherArgs& args, hipStream_t stream);
 hipError_t launch_write_page_table(const PageTableArgs& args, int n_records, hipStream_t stream);

@@ -31,9 +31,6 @@ constexpr unsigned kEventFlags = hipEventDisableTiming | hipEventDisableSystemFe
 constexpr size_t kPageRecordBytes = 4 * sizeof(int64_t);
 // one thread per gathered entry: a dispatch holds fewer than 2^32 work-items
 constexpr int64_t kMaxGather = INT32_MAX;
-// all-greedy batches with at least this many rows fill the GPU with one
-// workgroup per row and take the single-pass kernel; smaller ones split rows
-constexpr int kStreamGreedyMinRows = 256;
 
 struct DeviceGuard {
     int prev = -1;
@@ -57,9 +54,13 @@ struct dst_sampler {
     int dtype = 0;
     uint64_t seed = 0;
     int cus = 0;                       // compute units: stream blocks resident at once
-    void* workspace = nullptr;       // device: argmax slots and counters
-    uint64_t* slot = nullptr;
-    uint32_t* count = nullptr;
+    void* workspace = nullptr;       // device: split-row records, candidates and flags
+    dst::SplitRec* rec = nullptr;
+    uint64_t* cand = nullptr;
+    uint32_t* flags = nullptr;
+    int split_nl = 0;                  // loads per thread and chunk (0: rows go to the exact kernel)
+    int split_chunks = 0;              // chunks per row
+    uint32_t epoch = 0;                // last launch's publication epoch
     uint32_t* status_host = nullptr;  // pinned, mapped: device bounds-check flag
     uint32_t* status_dev = nullptr;
     hipEvent_t ring[kRing] = {};
@@ -154,17 +155,28 @@ int sampler_create(dst_sampler** out, int device, int32_t max_batch, int32_t voc
         s->cus = 0;                    // unknown: rows keep their index order
     }
 
-    const size_t slot_bytes = sizeof(uint64_t) * static_cast<size_t>(max_batch);
-    const size_t count_bytes = sizeof(uint32_t) * static_cast<size_t>(max_batch);
-    hipError_t e = hipMalloc(&s->workspace, slot_bytes + count_bytes);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        sampler_destroy(s);
-        return SAMPLER_ENOMEM;
+    // split-row workspace: per (row, chunk) a record and a candidate block,
+    // per row one cache line of epoch flags (zero: nothing published yet)
+    s->split_nl = dst::split_plan(vocab_size, logits_dtype, &s->split_chunks);
+    const size_t rows = static_cast<size_t>(max_batch);
+    const size_t nrec = rows * static_cast<size_t>(s->split_nl ? s->split_chunks : 0);
+    const size_t rec_bytes = nrec * sizeof(dst::SplitRec);
+    const size_t cand_bytes = nrec * dst::kSplitCap * sizeof(uint64_t);
+    const size_t flag_bytes = rows * dst::kSplitMaxChunks * sizeof(uint32_t);
+    hipError_t e = hipSuccess;
+    if (s->split_nl) {
+        e = hipMalloc(&s->workspace, rec_bytes + cand_bytes + flag_bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            sampler_destroy(s);
+            return SAMPLER_ENOMEM;
+        }
+        char* ws = static_cast<char*>(s->workspace);
+        s->rec = reinterpret_cast<dst::SplitRec*>(ws);
+        s->cand = reinterpret_cast<uint64_t*>(ws + rec_bytes);
+        s->flags = reinterpret_cast<uint32_t*>(ws + rec_bytes + cand_bytes);
+        e = hipMemset(s->flags, 0, flag_bytes);
     }
-    s->slot = static_cast<uint64_t*>(s->workspace);
-    s->count = reinterpret_cast<uint32_t*>(static_cast<char*>(s->workspace) + slot_bytes);
-    e = hipMemset(s->workspace, 0, slot_bytes + count_bytes);
     if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&s->status_host), sizeof(uint32_t),
                                            hipHostMallocMapped);
     if (e == hipSuccess) {
@@ -212,24 +224,7 @@ int sample_batch(dst_sampler* s, void* stream, const void* logits, int64_t row_s
     DeviceGuard g(s->device);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (!temperature && B < kStreamGreedyMinRows) {
-        dst::ArgmaxArgs a{};
-        a.logits = logits;
-        a.row_stride = row_stride;
-        a.B = B;
-        a.V = s->vocab;
-        dst::argmax_plan(B, s->vocab, s->dtype, &a.chunks, &a.chunk_len);
-        a.slot = s->slot;
-        a.count = s->count;
-        a.tokens_out = tokens_out;
-        if (dbg) {
-            a.probs_out = dbg->probs_out;
-            a.kept_out = dbg->kept_out;
-            a.topk_idx_out = dbg->topk_idx_out;
-            a.rand_out = dbg->rand_out;
-        }
-        e = dst::launch_argmax(a, s->dtype, st);
-    } else {
+    {
         dst::SampleArgs a{};
         a.logits = logits;
         a.row_stride = row_stride;
@@ -250,10 +245,23 @@ int sample_batch(dst_sampler* s, void* stream, const void* logits, int64_t row_s
             a.topk_idx_out = dbg->topk_idx_out;
             a.rand_out = dbg->rand_out;
         }
-        if (dbg && (dbg->flags & SAMPLER_DEBUG_FORCE_EXACT))
+        // the split-row kernel reads rows with 16-byte loads: the logits and
+        // every row start must be 16-byte aligned; other layouts, and
+        // vocabularies beyond its chunk count, take the exact kernel
+        const int64_t esize = s->dtype == SAMPLER_F32 ? 4 : 2;
+        const bool aligned = (reinterpret_cast<uintptr_t>(logits) & 15u) == 0 && ((row_stride * esize) & 15) == 0;
+        if ((dbg && (dbg->flags & SAMPLER_DEBUG_FORCE_EXACT)) || !s->split_nl || !aligned) {
             e = dst::launch_sample_exact(a, s->dtype, st);
-        else
-            e = dst::launch_sample_stream(a, s->dtype, st);
+        } else {
+            a.rec = s->rec;
+            a.cand = s->cand;
+            a.flags = s->flags;
+            a.rec_stride = s->split_chunks;
+            a.chunks = s->split_chunks;
+            s->epoch = s->epoch + 1u == 0u ? 1u : s->epoch + 1u;
+            a.epoch = s->epoch;
+            e = dst::launch_sample_split(a, s->dtype, s->split_nl, st);
+        }
     }
     if (e != hipSuccess) return fail(s, SAMPLER_EHIP, "sample_batch: launch", e);
     return SAMPLER_OK;
