@@ -32,13 +32,20 @@ struct SplitRec {
     double z;          // sum of the chunk's weights 2^(x c - rc)
     float rc;          // fl(m * c): the weights' reference
     uint32_t mode;
-    float seg[16];     // weight sums of the chunk's 16-byte-load slots
-    uint32_t pad[8];
+    // window of weight bins around the chunk's own top-p boundary (flat
+    // top-p chunks only; glo > ghi: none).  Bins are floor(16 x c), absolute.
+    float glo, ghi;
+    uint32_t wcnt;     // window elements published (after the candidates)
+    uint32_t above_n;  // elements in bins above ghi
+    double above_m;    // their weight (relative to rc)
+    uint32_t pad[18];
 };
 static_assert(sizeof(SplitRec) == 128, "record size");
 
 constexpr int kSplitThreads = 256;
 constexpr int kSplitCap = 256;        // candidates one chunk may publish
+constexpr int kSplitWinCap = 1024;    // window elements one chunk may publish
+constexpr int kSplitCandStride = kSplitCap + kSplitWinCap;   // entries per chunk block
 constexpr int kSplitMaxChunks = 64;   // chunks per row (one flag per lane of a wave)
 constexpr int kSplitXcds = 8;         // rows are dealt to the XCDs round robin
 
@@ -60,7 +67,7 @@ struct SampleArgs {
     uint64_t* rand_out;
     // split-row sampler workspace (see SplitRec)
     SplitRec* rec;             // [B][rec_stride]
-    uint64_t* cand;            // [B][rec_stride][kSplitCap] (order key << 32 | index)
+    uint64_t* cand;            // [B][rec_stride][kSplitCandStride] (order key << 32 | index)
     uint32_t* flags;           // [B][kSplitMaxChunks] epoch of the last publication
     int rec_stride;            // chunks allocated per row
     int chunks;                // chunks per row in this launch

@@ -12,44 +12,66 @@
 // 16-byte loads (thread t's load j covers chunk elements j*256*VEC + t*VEC +
 // [0, VEC)).  One 256-thread workgroup per chunk issues all of its loads at
 // once and keeps the chunk in registers, so every pass over the chunk after
-// the first is free of memory traffic and a CU keeps several chunks in flight.
-// The rows are dealt to the 8 XCDs round robin and a row's chunks are
-// consecutive workgroups of its XCD; the chunk dispatched last (S - 1)
-// finishes the row.
+// the first is free of memory traffic, and a CU keeps several chunks in
+// flight.  The rows are dealt to the 8 XCDs round robin and a row's chunks
+// are consecutive workgroups of its XCD; the chunk dispatched last (S - 1)
+// finishes the row.  Everything is inline (no calls, no scratch) and sized
+// for few registers, so that several workgroups share a CU.
 //
-// Every chunk publishes a record (chunk maximum and its lowest index, the
-// sum of its softmax weights per 16-byte-load slot, a candidate threshold)
-// and, for rows that select, every element at or above the threshold with its
-// index, in token order; then an epoch flag.  Publication uses device-scope
-// stores (written through the XCD's L2) and the flag follows only once the
-// data stores have completed (s_waitcnt), so a reader that sees the flag
-// with a device-scope load and then loads the data with device-scope loads
-// reads the published values.  The publishing workgroups never wait; only
-// the finisher polls the flags of its row, whose other chunks were
-// dispatched before it on the same XCD and therefore run.  Its wait is
-// bounded: past the limit it finishes the row by the exact routine, which
-// reads the row itself.
+// Every chunk publishes a record (its maximum and lowest index, the sum of
+// its softmax weights, a candidate threshold) and, for rows that select,
+// every element at or above the threshold with its index, in token order;
+// then an epoch flag.  Publication uses device-scope stores (written through
+// the XCD's L2), and the flag follows only once the data stores have
+// completed (s_waitcnt), so a reader that sees the flag with a device-scope
+// load and then loads the data with device-scope loads reads the published
+// values.  The publishing workgroups never wait; only the finisher polls the
+// flags of its row, whose other chunks were dispatched before it on the same
+// XCD and therefore run.  Its wait is bounded: past the limit it finishes
+// the row by the exact routine, which reads the row itself.
 //
-// Candidate thresholds.  For a rank target J (k for top-k rows, about 192
-// for top-p rows, 64 for the debug top-64), the chunk histograms its 16-byte
-// group maxima by distance below the chunk maximum (1/16 logit per bin) and
-// takes theta = the smallest group maximum in the bins that hold the J
-// largest.  J group maxima are J distinct elements >= theta, so the chunk's
-// J largest elements are all candidates; the union over the chunks holds
-// every element of the row at or above kappa = the largest chunk threshold,
-// which is at least the row's J largest.
+// Candidate thresholds.  For a rank target J (k for top-k rows, about
+// 1200/S for top-p rows, 64 for the debug top-64), the chunk histograms its
+// 16-byte group maxima by distance below the chunk maximum (1/16 logit per
+// bin) and takes theta = the smallest group maximum in the bins that hold
+// the J largest.  J group maxima are J distinct elements >= theta, so the
+// chunk's J largest elements are all candidates; the union over the chunks
+// holds every element of the row at or above kappa = the largest chunk
+// threshold.
+//
+// Flat top-p rows (a nucleus deeper than the candidates: high temperature or
+// logits without a dominant head).  A top-p chunk whose candidates hold less
+// than p of its own mass also histograms its weights in bins of 1/16 octave
+// (floor(16 x log2(e) / T), a grid common to every chunk of the row), finds
+// the bin where its own descending mass reaches p, and publishes the
+// elements of a window of bins around it (grown while it holds at most about
+// 768 elements, so narrow where the row is dense) with the mass and count of
+// everything above the window.  The row's boundary bin lies between the
+// smallest and the largest of the chunks' own boundary bins; when it lies in
+// every chunk's window, the finisher locates it from the published elements
+// and masses and resolves the cut inside it.
 //
 // The finisher loads the candidates >= kappa into LDS (in token order) and
 // finds cuts by descents over key histograms (by count for top-k, by mass
-// for top-p), resolving the boundary bin exactly; it draws by a block-wide
-// scan of the kept weights in token order.  Rows with no filter draw from
-// the per-slot weight sums and re-read one 16-byte-load slot of one chunk.
-// Whatever the candidates cannot settle (a nucleus reaching below kappa, a
-// chunk with too many candidates, a top-k too large to aim at) is finished
-// by the exact multi-pass routine over the whole row.
+// for top-p), resolving the boundary bin exactly.  Rows whose kept set is in
+// the list draw by a block-wide scan of the kept weights in token order;
+// rows with no filter and flat rows find the chunk holding the target from
+// the published masses and re-read that one chunk.  Whatever the published
+// data cannot settle is finished by the exact multi-pass routine over the
+// whole row.
 #include "device_common.hpp"
 #include "exact_path.hpp"
 #include "kernels.hpp"
+
+#ifndef DST_SPLIT_NL_F32
+#define DST_SPLIT_NL_F32 16     // 16-byte loads per thread and chunk, fp32 rows
+#endif
+#ifndef DST_SPLIT_NL_BF16
+#define DST_SPLIT_NL_BF16 16    // ... bf16 rows
+#endif
+#ifndef DST_SPLIT_WAVES_PER_EU
+#define DST_SPLIT_WAVES_PER_EU 5
+#endif
 
 namespace dst {
 
@@ -57,50 +79,61 @@ namespace {
 
 constexpr int kT = kSplitThreads;
 constexpr int kNW = kT / kWave;
-constexpr int kBins = 1024;
-constexpr int kListMax = 2048;        // candidates the finisher holds
+constexpr int kGBins = 1024;          // group-maximum histogram: 1/16 logit per bin
+constexpr int kDBins = 512;           // descent histograms
+constexpr int kHBins = 512;           // flat chunks: weight histogram, 1/16 octave per bin
+constexpr int kWinBudget = 768;       // elements a flat chunk's window aims to hold
+constexpr int kListMax = 1536;        // candidates the finisher holds
 constexpr int kKList = 128;           // top-k rows up to this k aim their thresholds at k
-constexpr int kJTopP = 192;           // rank aimed at by top-p / min_p rows
+constexpr int kPList = 1200;          // top-p / min_p rows: candidates aimed at per row
 constexpr int kJMax = 224;            // largest rank aimed at (a chunk publishes <= kSplitCap)
 constexpr int kJDebug = 64;           // debug: the row's 64 largest
 constexpr float kGroupBinScale = 16.0f;
+constexpr float kWeightBinScale = 16.0f;
 constexpr int kSpinLimit = 1 << 16;
 constexpr int kSmall = 64;
 
 enum : uint32_t { kModeArgmax = 0, kModeTopK = 1, kModeTopP = 2, kModeFull = 3, kModeExact = 4 };
 
 static_assert(kT == 256 && kNW == 4, "the block layout below assumes 4 waves");
-static_assert(kListMax == 8 * kT, "eight list entries per thread");
 
 struct ChunkSmem {
-    uint32_t hist[kBins];
-    double wsum[kNW][16];
+    uint32_t gh[kGBins];
+    float wh[kHBins];
+    uint32_t wcn[kHBins];
     uint32_t wtot[kNW][16];
     uint32_t off[kNW][16];
-    float fseg[16];
+    double dred[kNW][8];
+    uint32_t ured32[kNW][8];
     float fred[kNW];
     uint64_t ured[kNW];
-    uint32_t bsel;
-    uint32_t total;
+    uint32_t bsel, total;
+    int rsel, rlo, rhi;
 };
 
 struct FinSmem {
     uint32_t key[kListMax];
     uint32_t idx[kListMax];
     float w[kListMax];
-    uint32_t hcnt[kBins];
-    double hmass[kBins];
+    uint32_t hcnt[kDBins];
+    double hmass[kDBins];
     float cm[kSplitMaxChunks];
     uint32_t camax[kSplitMaxChunks];
     float ctheta[kSplitMaxChunks];
     uint32_t ccnt[kSplitMaxChunks];
     double cz[kSplitMaxChunks];
     float crc[kSplitMaxChunks];
+    double csc[kSplitMaxChunks];       // 2^(rc_c - rref)
+    float cglo[kSplitMaxChunks], cghi[kSplitMaxChunks];
+    uint32_t cwcnt[kSplitMaxChunks];
+    double ckept[kSplitMaxChunks];     // flat rows: kept mass per chunk
     uint32_t coff[kSplitMaxChunks + 1];
     uint32_t skey[kSmall];
     uint32_t sidx[kSmall];
     float sw[kSmall];
     uint32_t sn;
+    double slot[kNW][16];
+    double slott[16];
     // block scan scratch
     uint32_t wc[kNW];
     double wm[kNW];
@@ -112,10 +145,10 @@ struct FinSmem {
     int32_t tok;
     int32_t last;
     uint32_t list_n, kappa, maxkey, bad;
-    double zrow;
-    int cstar, jstar;
-    double before;
-    int next;
+    double zrow, before, amass;
+    uint32_t anum;
+    float gstar, gwlo, gwhi;
+    int cstar, jstar, next;
 };
 
 union SplitSmem {
@@ -166,14 +199,25 @@ __device__ __forceinline__ float wave_min_dpp(float v) {
     return __uint_as_float(readlane_u32(__float_as_uint(v), 63));
 }
 
+__device__ __forceinline__ uint32_t wave_sum_u32_dpp(uint32_t v) {
+    return readlane_u32(wave_scan_u32_dpp(v), 63);
+}
+
+typedef uint32_t u32x4_t_ __attribute__((ext_vector_type(4)));
+
 // Makes the compiler treat the chunk registers as changed: values derived
 // from them in one pass (unpacked bf16, keys) are recomputed in the next
 // instead of being kept live across it.
 template <int NL>
-__device__ __forceinline__ void opaque(uint4 (&d)[NL]) {
+__device__ __forceinline__ void opaque(u32x4_t_ (&d)[NL]) {
 #pragma unroll
-    for (int j = 0; j < NL; ++j) __asm__ __volatile__("" : "+v"(d[j].x), "+v"(d[j].y), "+v"(d[j].z), "+v"(d[j].w));
+    for (int j = 0; j < NL; ++j) __asm__ __volatile__("" : "+v"(d[j]));
 }
+
+// Keeps the scheduler from moving work across it: placed after each 16-byte
+// slot of a pass, it bounds the values in flight to one slot's (without it
+// the whole chunk's exponents are hoisted ahead of their sums and spill).
+__device__ __forceinline__ void slot_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return static_cast<int>(threadIdx.x) >> 6; }
@@ -213,7 +257,7 @@ __device__ __forceinline__ void block_scan2(uint32_t c, double m, uint32_t* ec, 
 // ----------------------------------------------------------- the chunk --
 
 template <int DT>
-__device__ __forceinline__ float elem(const uint4& v, int e) {
+__device__ __forceinline__ float elem(const u32x4_t_& v, int e) {
     if (DT == kDtypeF32) {
         const uint32_t w = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
         return __uint_as_float(w);
@@ -261,20 +305,148 @@ __device__ __forceinline__ const char* row_ptr(const SampleArgs& a, int b, int e
     return static_cast<const char*>(a.logits) + static_cast<int64_t>(b) * a.row_stride * es;
 }
 
+// The chunk into registers.  Every 16-byte slot is a buffer load through a
+// descriptor bounded by the row, issued without a branch (a load past the row
+// returns zeros and is replaced by -inf), so all NL loads are in flight
+// before the first wait; the non-temporal hint keeps the row, read once,
+// from displacing other lines.  The slot that straddles V (V not a multiple
+// of VEC) is re-read element by element afterwards.
+template <int DT, int NL>
+__device__ __forceinline__ void load_chunk(const SampleArgs& a, int b, int c, u32x4_t_ (&d)[NL]) {
+    using G = Geo<DT, NL>;
+    constexpr int VEC = G::VEC;
+    constexpr int kNonTemporal = 2;
+    const char* rowp = row_ptr(a, b, G::ES);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(rowp), static_cast<short>(0), a.V * G::ES, 0x00020000);
+    const uint32_t pad = DT == kDtypeF32 ? 0xff800000u : 0xff80ff80u;
+    // element offsets fit 32 bits: a row has at most kSplitMaxChunks chunks.
+    // One vector offset for the thread; slot j adds the constant j * SLOT,
+    // passed as the scalar offset.  Slots 0 .. jfull lie inside the row.
+    const int base = c * static_cast<int>(G::ELEMS) + static_cast<int>(threadIdx.x) * VEC;
+    const int room = a.V - VEC - base;
+    const int jfull = room < 0 ? -1 : room / G::SLOT;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const u32x4_t_ v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, base * G::ES, j * G::SLOT * G::ES,
+                                                                 kNonTemporal);
+        const bool full = j <= jfull;
+        d[j] = full ? v : u32x4_t_{pad, pad, pad, pad};
+    }
+    if (a.V % VEC != 0) {
+        // the one slot that straddles V, if it is this thread's
+        const int rest = a.V - base;
+        const int jp = rest > 0 && rest % G::SLOT < VEC && rest % G::SLOT > 0 ? rest / G::SLOT : -1;
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+            if (j == jp) {
+                const uint4 v = load_slot<DT>(rowp, a.V, base + j * G::SLOT);
+                d[j] = u32x4_t_{v.x, v.y, v.z, v.w};
+            }
+    }
+}
+
+// The common weight-bin grid of a row: floor(16 x log2(e) / T).
+__device__ __forceinline__ float weight_bin(float x, float cc) {
+    return floorf(x * cc * kWeightBinScale);
+}
+
+// Block sum of a double in a fixed order (wave trees, then the waves in
+// order); `slot` picks the scratch column, which stays valid until reused.
+__device__ __forceinline__ double block_sum_f64(double v, ChunkSmem& sm, int slot) {
+    const double w = wave_sum_dpp(v);
+    if (lane_id() == 0) sm.dred[wave_id()][slot] = w;
+    __syncthreads();
+    return sm.dred[0][slot] + sm.dred[1][slot] + sm.dred[2][slot] + sm.dred[3][slot];
+}
+
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, ChunkSmem& sm, int slot) {
+    const uint32_t w = wave_sum_u32_dpp(v);
+    if (lane_id() == 0) sm.ured32[wave_id()][slot] = w;
+    __syncthreads();
+    return sm.ured32[0][slot] + sm.ured32[1][slot] + sm.ured32[2][slot] + sm.ured32[3][slot];
+}
+
 // The chunk's part of the row: loads it, reduces it and publishes its record
 // and candidates (see the file comment).  mode is the row's route, cc the
-// fp32 log2(e)/T, jrank the candidate rank target (0: none).
+// fp32 log2(e)/T, jrank the candidate rank target scaled by the chunk's
+// length, jmin the rank every chunk covers; flat_p > 0 enables the window of
+// flat top-p chunks (the row's top-p).
+// Ordered compaction: the chunk's elements that pass keep(x), in token order
+// (per slot, those of lower threads first; slot counts travel two to a
+// register through the wave scan), written as (order key << 32 | index) to
+// out[0, total) when total <= cap; each(x) sees every written element.
+// Returns total, the same in every thread.
+template <int DT, int NL, typename P, typename E>
+__device__ __forceinline__ uint32_t ordered_publish(u32x4_t_ (&d)[NL], ChunkSmem& sm, uint32_t tbase, uint64_t* out,
+                                                    uint32_t cap, P keep, E each) {
+    using G = Geo<DT, NL>;
+    constexpr int VEC = G::VEC;
+    static_assert(NL % 2 == 0, "slot counts are paired");
+    const int t = static_cast<int>(threadIdx.x), lane = lane_id(), wid = wave_id();
+    uint32_t exq[NL / 2];
+#pragma unroll
+    for (int q = 0; q < NL / 2; ++q) {
+        uint32_t n0 = 0, n1 = 0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            n0 += keep(elem<DT>(d[2 * q], e)) ? 1u : 0u;
+            n1 += keep(elem<DT>(d[2 * q + 1], e)) ? 1u : 0u;
+        }
+        const uint32_t pk = n0 | (n1 << 16);
+        const uint32_t in = wave_scan_u32_dpp(pk);
+        exq[q] = in - pk;
+        if (lane == kWave - 1) {
+            sm.wtot[wid][2 * q] = in & 0xffffu;
+            sm.wtot[wid][2 * q + 1] = in >> 16;
+        }
+    }
+    opaque(d);
+    __syncthreads();
+    if (t == 0) {
+        uint32_t run = 0;
+        for (int j = 0; j < NL; ++j) {
+            for (int w = 0; w < kNW; ++w) {
+                sm.off[w][j] = run;
+                run += sm.wtot[w][j];
+            }
+            slot_fence();
+        }
+        sm.total = run;
+    }
+    __syncthreads();
+    const uint32_t total = sm.total;
+    if (total <= cap) {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            uint32_t pos = sm.off[wid][j] + ((exq[j / 2] >> ((j & 1) * 16)) & 0xffffu);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float x = elem<DT>(d[j], e);
+                if (keep(x)) {
+                    st_dev(out + pos, (static_cast<uint64_t>(f32_key(x)) << 32) | (tbase + j * G::SLOT + e));
+                    ++pos;
+                    each(x);
+                }
+            }
+            slot_fence();
+        }
+    }
+    opaque(d);
+    __syncthreads();   // sm.total and sm.off may be reused
+    return total;
+}
+
 template <int DT, int NL>
 __device__ __forceinline__ void chunk_phase(const SampleArgs& a, ChunkSmem& sm, int b, int c, uint32_t mode,
-                                            float cc, int jrank, int jmin) {
+                                            float cc, int jrank, int jmin, float flat_p) {
     using G = Geo<DT, NL>;
     constexpr int VEC = G::VEC;
     const int t = static_cast<int>(threadIdx.x), lane = lane_id(), wid = wave_id();
-    const char* rowp = row_ptr(a, b, G::ES);
-    const int64_t base = static_cast<int64_t>(c) * G::ELEMS;
-    uint4 d[NL];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) d[j] = load_slot<DT>(rowp, a.V, base + static_cast<int64_t>(j) * G::SLOT + t * VEC);
+    const int base = c * static_cast<int>(G::ELEMS);
+    const uint32_t tbase = static_cast<uint32_t>(base + t * VEC);
+    u32x4_t_ d[NL];
+    load_chunk<DT, NL>(a, b, c, d);
 
     SplitRec* rec = a.rec + static_cast<int64_t>(b) * a.rec_stride + c;
 
@@ -291,9 +463,10 @@ __device__ __forceinline__ void chunk_phase(const SampleArgs& a, ChunkSmem& sm, 
         for (int j = NL - 1; j >= 0; --j) {
 #pragma unroll
             for (int e = VEC - 1; e >= 0; --e) {
-                const uint32_t i = static_cast<uint32_t>(base + j * G::SLOT + t * VEC + e);
+                const uint32_t i = (tbase + j * G::SLOT + e);
                 ti = elem<DT>(d[j], e) == tm ? i : ti;
             }
+            slot_fence();
         }
         const uint64_t pk = (static_cast<uint64_t>(f32_key(tm)) << 32) | static_cast<uint64_t>(0xffffffffu - ti);
         const uint64_t wb = wave_max_u64_dpp(pk);
@@ -322,71 +495,68 @@ __device__ __forceinline__ void chunk_phase(const SampleArgs& a, ChunkSmem& sm, 
 #pragma unroll
     for (int j = 0; j < NL; ++j) tm = fmaxf(tm, group_max(j));
     opaque(d);
-
-    // chunk maximum
     const float wmax = wave_max_dpp(tm);
     if (lane == 0) sm.fred[wid] = wmax;
     __syncthreads();
     const float mc = fmaxf(fmaxf(sm.fred[0], sm.fred[1]), fmaxf(sm.fred[2], sm.fred[3]));
 
-    // softmax weights 2^(x c - rc) summed per load slot: fp32 over the
-    // thread's VEC elements, fp64 across the block
+    // softmax weights 2^(x c - rc): fp32 over the thread's elements, fp64
+    // across the block
     const float rc = mc * cc;
+    double z = 0.0;
     if (mode == kModeTopP || mode == kModeFull) {
+        float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
-            float s = 0.0f;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) s += __builtin_amdgcn_exp2f(fmaf(elem<DT>(d[j], e), cc, -rc));
-            const double ws = wave_sum_dpp(static_cast<double>(s));
-            if (lane == 0) sm.wsum[wid][j] = ws;
+            for (int e = 0; e < VEC; ++e) {
+                const float w = __builtin_amdgcn_exp2f(fmaf(elem<DT>(d[j], e), cc, -rc));
+                if (e & 1) s1 += w; else s0 += w;
+            }
+            slot_fence();
         }
-        __syncthreads();
-        if (t < NL) {
-            const double sj = sm.wsum[0][t] + sm.wsum[1][t] + sm.wsum[2][t] + sm.wsum[3][t];
-            sm.fseg[t] = static_cast<float>(sj);
-            st_dev_f32(&rec->seg[t], static_cast<float>(sj));
-        }
-        __syncthreads();
+        opaque(d);
+        z = block_sum_f64(static_cast<double>(s0) + static_cast<double>(s1), sm, 0);
     }
 
     float theta = INFINITY;
     uint32_t total = 0;
+    double cand_mass = 0.0;
     if (jrank > 0) {
+        const int64_t valid = a.V - base < G::ELEMS ? a.V - base : G::ELEMS;   // elements in the chunk
+        const int64_t scaled = (static_cast<int64_t>(jrank) * valid + G::ELEMS - 1) / G::ELEMS;
+        const uint32_t J = static_cast<uint32_t>(scaled > jmin ? scaled : jmin);
         // histogram of the group maxima by distance below the chunk maximum
-        for (int i = t; i < kBins; i += kT) sm.hist[i] = 0u;
+        for (int i = t; i < kGBins; i += kT) sm.gh[i] = 0u;
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             const float g = group_max(j);
             if (g > -INFINITY) {
-                const uint32_t bin = static_cast<uint32_t>(fminf((mc - g) * kGroupBinScale, 1023.0f));
-                atomicAdd(&sm.hist[bin], 1u);
+                const uint32_t bin = static_cast<uint32_t>(fminf((mc - g) * kGroupBinScale, kGBins - 1.0f));
+                atomicAdd(&sm.gh[bin], 1u);
             }
+            slot_fence();
         }
         opaque(d);
         __syncthreads();
-        // the bin holding the jrank-th largest (thread t owns bins 4t .. 4t+3)
+        // the bin holding the J-th largest (thread t owns bins 4t .. 4t+3)
         uint32_t h[4], own = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            h[q] = sm.hist[4 * t + q];
+            h[q] = sm.gh[4 * t + q];
             own += h[q];
         }
         const uint32_t incl = wave_scan_u32_dpp(own);
         if (lane == kWave - 1) sm.wtot[wid][0] = incl;
-        if (t == 0) sm.bsel = kBins - 1;
+        if (t == 0) sm.bsel = kGBins - 1;
         __syncthreads();
         uint32_t excl = incl - own, groups = 0;
+#pragma unroll
         for (int w = 0; w < kNW; ++w) {
             excl += w < wid ? sm.wtot[w][0] : 0u;
             groups += sm.wtot[w][0];
         }
-        // the rank aimed at scales with the chunk's length (the last chunk of a
-        // row may be short), never below jmin (a top-k set may lie in one chunk)
-        const int64_t valid = a.V - base < G::ELEMS ? a.V - base : G::ELEMS;
-        const int64_t scaled = (static_cast<int64_t>(jrank) * valid + G::ELEMS - 1) / G::ELEMS;
-        const uint32_t J = static_cast<uint32_t>(scaled > jmin ? scaled : jmin);
         if (excl < J && excl + own >= J) {
             uint32_t cum = excl;
 #pragma unroll
@@ -415,73 +585,132 @@ __device__ __forceinline__ void chunk_phase(const SampleArgs& a, ChunkSmem& sm, 
             for (int j = 0; j < NL; ++j) {
                 const float g = group_max(j);
                 if (g > -INFINITY) {
-                    const uint32_t bin = static_cast<uint32_t>(fminf((mc - g) * kGroupBinScale, 1023.0f));
+                    const uint32_t bin = static_cast<uint32_t>(fminf((mc - g) * kGroupBinScale, kGBins - 1.0f));
                     if (bin <= bsel) tmin = fminf(tmin, g);
                 }
+                slot_fence();
             }
         }
+        opaque(d);
         const float wmin = wave_min_dpp(tmin);
         if (lane == 0) sm.fred[wid] = wmin;
         __syncthreads();
         theta = fminf(fminf(sm.fred[0], sm.fred[1]), fminf(sm.fred[2], sm.fred[3]));
 
-        opaque(d);
-        // ordered compaction: per slot, the candidates of lower threads first;
-        // slot counts travel two to a register through the wave scan
-        uint32_t exq[NL / 2];
+        float cm32 = 0.0f;
+        total = ordered_publish<DT, NL>(
+            d, sm, tbase, a.cand + (static_cast<int64_t>(b) * a.rec_stride + c) * kSplitCandStride,
+            static_cast<uint32_t>(kSplitCap), [&](float x) { return x >= theta; },
+            [&](float x) { cm32 += __builtin_amdgcn_exp2f(fmaf(x, cc, -rc)); });
+        if (flat_p > 0.0f) cand_mass = block_sum_f64(static_cast<double>(cm32), sm, 1);
+    }
+
+    // flat top-p chunk: the window of weight bins around its own boundary
+    float glo = 1.0f, ghi = 0.0f;
+    if (flat_p > 0.0f && total <= static_cast<uint32_t>(kSplitCap) && cand_mass < static_cast<double>(flat_p) * z) {
+        for (int i = t; i < kHBins; i += kT) {
+            sm.wh[i] = 0.0f;
+            sm.wcn[i] = 0u;
+        }
+        if (t == 0) sm.rsel = -1;
+        __syncthreads();
+        const float gtop = weight_bin(mc, cc);
 #pragma unroll
-        for (int q = 0; q < NL / 2; ++q) {
-            opaque(d);
-            uint32_t n0 = 0, n1 = 0;
+        for (int j = 0; j < NL; ++j) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                n0 += elem<DT>(d[2 * q], e) >= theta ? 1u : 0u;
-                n1 += elem<DT>(d[2 * q + 1], e) >= theta ? 1u : 0u;
-            }
-            const uint32_t pk = n0 | (n1 << 16);
-            const uint32_t in = wave_scan_u32_dpp(pk);
-            exq[q] = in - pk;
-            if (lane == kWave - 1) {
-                sm.wtot[wid][2 * q] = in & 0xffffu;
-                sm.wtot[wid][2 * q + 1] = in >> 16;
-            }
-        }
-        __syncthreads();
-        if (t == 0) {
-            uint32_t run = 0;
-            for (int j = 0; j < NL; ++j) {
-                for (int w = 0; w < kNW; ++w) {
-                    sm.off[w][j] = run;
-                    run += sm.wtot[w][j];
+                const float x = elem<DT>(d[j], e);
+                if (x > -INFINITY) {
+                    const int r = static_cast<int>(fminf(gtop - weight_bin(x, cc), kHBins - 1.0f));
+                    atomicAdd(&sm.wh[r], __builtin_amdgcn_exp2f(fmaf(x, cc, -rc)));
+                    atomicAdd(&sm.wcn[r], 1u);
                 }
             }
-            sm.total = run;
+            slot_fence();
+        }
+        opaque(d);
+        __syncthreads();
+        // the bin where the descending mass reaches flat_p of the chunk's
+        // (thread t owns bins 2t, 2t + 1)
+        const double target = static_cast<double>(flat_p) * z;
+        const double h0 = sm.wh[2 * t], h1 = sm.wh[2 * t + 1];
+        const double inc = wave_scan_f64_dpp(h0 + h1);
+        if (lane == kWave - 1) sm.dred[wid][2] = inc;
+        __syncthreads();
+        double ex = inc - (h0 + h1);
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) ex += w < wid ? sm.dred[w][2] : 0.0;
+        if (ex < target && ex + h0 >= target) sm.rsel = 2 * t;
+        else if (ex + h0 < target && ex + h0 + h1 >= target) sm.rsel = 2 * t + 1;
+        __syncthreads();
+        if (t == 0) {
+            // grow the window from that bin, one bin up and one down in turn,
+            // while it holds at most kWinBudget elements; the deepest bin (all
+            // the deeper weights) never belongs to it
+            const int rs = sm.rsel;
+            int lo = rs, hi = rs;
+            uint32_t cnt = rs >= 0 ? sm.wcn[rs] : 0u;
+            bool up = true, down = true;
+            while (rs >= 0 && (up || down)) {
+                if (up) {
+                    up = lo > 0 && cnt + sm.wcn[lo - 1] <= static_cast<uint32_t>(kWinBudget);
+                    if (up) cnt += sm.wcn[--lo];
+                }
+                if (down) {
+                    down = hi + 1 < kHBins - 1 && cnt + sm.wcn[hi + 1] <= static_cast<uint32_t>(kWinBudget);
+                    if (down) cnt += sm.wcn[++hi];
+                }
+            }
+            const bool usable = rs >= 0 && hi < kHBins - 1 && cnt <= static_cast<uint32_t>(kSplitWinCap);
+            sm.rlo = usable ? lo : -1;
+            sm.rhi = hi;
         }
         __syncthreads();
-        total = sm.total;
-        opaque(d);
-        if (total <= static_cast<uint32_t>(kSplitCap)) {
-            uint64_t* out = a.cand + (static_cast<int64_t>(b) * a.rec_stride + c) * kSplitCap;
+        if (sm.rlo >= 0) {
+            glo = gtop - static_cast<float>(sm.rhi);
+            ghi = gtop - static_cast<float>(sm.rlo);
+            // everything above the window: its mass and count
+            float am = 0.0f;
+            uint32_t an = 0;
 #pragma unroll
             for (int j = 0; j < NL; ++j) {
-                opaque(d);
-                uint32_t pos = sm.off[wid][j] + ((exq[j / 2] >> ((j & 1) * 16)) & 0xffffu);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
                     const float x = elem<DT>(d[j], e);
-                    if (x >= theta) {
-                        const uint32_t i = static_cast<uint32_t>(base + j * G::SLOT + t * VEC + e);
-                        st_dev(out + pos, (static_cast<uint64_t>(f32_key(x)) << 32) | i);
-                        ++pos;
+                    if (x > -INFINITY && weight_bin(x, cc) > ghi) {
+                        am += __builtin_amdgcn_exp2f(fmaf(x, cc, -rc));
+                        ++an;
                     }
                 }
+                slot_fence();
+            }
+            opaque(d);
+            const double am_b = block_sum_f64(static_cast<double>(am), sm, 3);
+            const uint32_t an_b = block_sum_u32(an, sm, 0);
+            // the window's elements, in token order (their masses are derived
+            // by the finisher)
+            const float wlo = glo, whi = ghi;
+            const uint32_t wn = ordered_publish<DT, NL>(
+                d, sm, tbase,
+                a.cand + (static_cast<int64_t>(b) * a.rec_stride + c) * kSplitCandStride + kSplitCap,
+                static_cast<uint32_t>(kSplitWinCap),
+                [&](float x) {
+                    const float g = weight_bin(x, cc);
+                    return x > -INFINITY && g >= wlo && g <= whi;
+                },
+                [](float) {});
+            if (wn > static_cast<uint32_t>(kSplitWinCap)) {
+                glo = 1.0f;
+                ghi = 0.0f;
+            } else if (t == 0) {
+                st_dev(&rec->wcnt, wn);
+                st_dev_f64(&rec->above_m, am_b);
+                st_dev(&rec->above_n, an_b);
             }
         }
     }
+
     if (t == 0) {
-        double z = 0.0;
-        if (mode == kModeTopP || mode == kModeFull)
-            for (int j = 0; j < NL; ++j) z += static_cast<double>(sm.fseg[j]);
         st_dev_f64(&rec->z, z);
         st_dev_f32(&rec->m, mc);
         st_dev(&rec->amax, 0u);
@@ -489,6 +718,8 @@ __device__ __forceinline__ void chunk_phase(const SampleArgs& a, ChunkSmem& sm, 
         st_dev(&rec->cnt, jrank > 0 ? (total <= static_cast<uint32_t>(kSplitCap) ? total : kSplitCap + 1u) : 0u);
         st_dev_f32(&rec->rc, rc);
         st_dev(&rec->mode, mode);
+        st_dev_f32(&rec->glo, glo);
+        st_dev_f32(&rec->ghi, ghi);
     }
 }
 
@@ -505,7 +736,7 @@ __device__ __forceinline__ bool kept_by(const DCut& c, uint32_t k, uint32_t i) {
 struct Found {
     bool ok;
     DCut cut;
-    uint32_t n;       // entries kept (within the restriction)
+    uint32_t n;       // entries kept (within the restriction, plus above_n0)
 };
 
 // Sorts the small list (n <= 64 entries in f.skey/sidx/sw) into descending
@@ -524,8 +755,6 @@ __device__ __forceinline__ void small_sorted(FinSmem& f, uint32_t n, uint32_t* k
         const uint32_t ok = f.skey[q], oi = f.sidx[q];
         rank += (ok > mk || (ok == mk && oi < mi)) ? 1u : 0u;
     }
-    // scatter by rank through the LDS list itself (wave 0 only; the
-    // lanes read back in rank order)
     __builtin_amdgcn_wave_barrier();
     if (lane < static_cast<int>(n)) {
         f.skey[rank] = mk;
@@ -540,19 +769,22 @@ __device__ __forceinline__ void small_sorted(FinSmem& f, uint32_t n, uint32_t* k
 
 // Cut after the first `target_n` entries (COUNT) or after the entries whose
 // exclusive prefix mass is below `target_m` (MASS), in descending order,
-// among the active entries (key >= lo0) kept by `res`.  Block-uniform.
+// among the active entries (key >= lo0) kept by `res`; the prefix starts at
+// (above_n0, above_m0), the count and mass of what lies above every entry.
+// Block-uniform.
 template <bool MASS>
-__device__ __forceinline__ Found descent(FinSmem& f, int L, uint32_t lo0, uint32_t hi0, DCut res, uint32_t target_n,
-                         double target_m) {
+__device__ __forceinline__ Found descent(FinSmem& f, int L, uint32_t lo0, uint32_t hi0, DCut res,
+                                         uint32_t target_n, double target_m, uint32_t above_n0 = 0,
+                                         double above_m0 = 0.0) {
     const int t = static_cast<int>(threadIdx.x);
     uint32_t lo = lo0, hi = hi0;
-    uint32_t above_n = 0;
-    double above_m = 0.0;
-    for (int round = 0; round < 6; ++round) {
+    uint32_t above_n = above_n0;
+    double above_m = above_m0;
+    for (int round = 0; round < 8; ++round) {
         const uint32_t span = hi - lo;
         int sh = 0;
-        while ((span >> sh) >= static_cast<uint32_t>(kBins)) ++sh;
-        for (int i = t; i < kBins; i += kT) {
+        while ((span >> sh) >= static_cast<uint32_t>(kDBins)) ++sh;
+        for (int i = t; i < kDBins; i += kT) {
             f.hcnt[i] = 0u;
             if (MASS) f.hmass[i] = 0.0;
         }
@@ -566,12 +798,12 @@ __device__ __forceinline__ Found descent(FinSmem& f, int L, uint32_t lo0, uint32
             if (MASS) atomicAdd(&f.hmass[bin], static_cast<double>(f.w[i]));
         }
         __syncthreads();
-        // thread t owns bins 1023 - 4t - q, q = 0..3 (descending)
-        uint32_t hc[4], oc = 0;
-        double hm[4], om = 0.0;
+        // thread t owns bins kDBins - 1 - 2t - q, q = 0, 1 (descending)
+        uint32_t hc[2], oc = 0;
+        double hm[2], om = 0.0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int bin = kBins - 1 - 4 * t - q;
+        for (int q = 0; q < 2; ++q) {
+            const int bin = kDBins - 1 - 2 * t - q;
             hc[q] = f.hcnt[bin];
             hm[q] = MASS ? f.hmass[bin] : 0.0;
             oc += hc[q];
@@ -583,11 +815,11 @@ __device__ __forceinline__ Found descent(FinSmem& f, int L, uint32_t lo0, uint32
         uint32_t cum_c = above_n + ec;
         double cum_m = above_m + em;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 2; ++q) {
             const bool hit = MASS ? (cum_m < target_m && cum_m + hm[q] >= target_m)
                                   : (cum_c < target_n && cum_c + hc[q] >= target_n);
             if (hit) {
-                f.sel_bin = kBins - 1 - 4 * t - q;
+                f.sel_bin = kDBins - 1 - 2 * t - q;
                 f.sel_c = cum_c;
                 f.sel_m = cum_m;
                 f.sel_cnt = hc[q];
@@ -665,12 +897,8 @@ __device__ __forceinline__ Found descent(FinSmem& f, int L, uint32_t lo0, uint32
             }
             uint32_t ec2, tc2;
             double em2, tm2;
-            if (t == 0) {
-                f.res_ok = 0u;
-            }
+            if (t == 0) f.res_ok = 0u;
             block_scan2(oc2, om2, &ec2, &em2, &tc2, &tm2, f);
-            // COUNT: the (target_n - sel_c)-th tie; MASS: the last tie whose
-            // exclusive prefix is below the target
             uint32_t run_c = ec2;
             double run_m = sel_m + em2;
             const uint32_t need = target_n - sel_c;
@@ -713,8 +941,8 @@ __device__ __forceinline__ Found descent(FinSmem& f, int L, uint32_t lo0, uint32
 
 // Writes the first n entries of the descending order (n <= 64) as the debug
 // top-k index list: the n entries kept by the count cut, sorted in wave 0.
-__device__ __forceinline__ void debug_topk_list(const SampleArgs& a, int b, FinSmem& f, int L, uint32_t kappa, uint32_t maxkey,
-                                uint32_t n) {
+__device__ __forceinline__ void debug_topk_list(const SampleArgs& a, int b, FinSmem& f, int L, uint32_t kappa,
+                                                uint32_t maxkey, uint32_t n) {
     const int t = static_cast<int>(threadIdx.x);
     int32_t* o = a.topk_idx_out + static_cast<int64_t>(b) * kDebugTopK;
     const Found fc = descent<false>(f, L, kappa, maxkey, DCut{0u, 0xffffffffu}, n, 0.0);
@@ -743,41 +971,127 @@ __device__ __forceinline__ void debug_topk_list(const SampleArgs& a, int b, FinS
     __syncthreads();
 }
 
-// Debug: the final distribution over the whole row.  kept(c, i, key) says
-// whether element i is kept; weight(c, x) returns its weight (divided by W).
+// Debug: the final distribution over the whole row.  kept(i, x, key) says
+// whether element i is kept; weight(c, x) returns its probability.
 template <int DT, int NL, typename K, typename Wt>
 __device__ __forceinline__ void debug_probs(const SampleArgs& a, int b, K kept, Wt weight) {
     using G = Geo<DT, NL>;
     constexpr int VEC = G::VEC;
-    const char* rowp = row_ptr(a, b, G::ES);
     float* pr = a.probs_out + static_cast<int64_t>(b) * a.V;
     const int t = static_cast<int>(threadIdx.x);
     for (int c = 0; c < a.chunks; ++c) {
-        const int64_t base = static_cast<int64_t>(c) * G::ELEMS;
-        uint4 d[NL];
-#pragma unroll
-        for (int j = 0; j < NL; ++j) d[j] = load_slot<DT>(rowp, a.V, base + static_cast<int64_t>(j) * G::SLOT + t * VEC);
+        const uint32_t tbase = static_cast<uint32_t>(c * static_cast<int>(G::ELEMS) + t * VEC);
+        u32x4_t_ d[NL];
+        load_chunk<DT, NL>(a, b, c, d);
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const int64_t i = base + static_cast<int64_t>(j) * G::SLOT + t * VEC + e;
-                if (i >= a.V) continue;
+                const uint32_t i = tbase + j * G::SLOT + e;
+                if (i >= static_cast<uint32_t>(a.V)) continue;
                 const float x = elem<DT>(d[j], e);
-                const uint32_t k = f32_key(x);
-                pr[i] = kept(c, static_cast<uint32_t>(i), k) ? weight(c, x) : 0.0f;
+                pr[i] = kept(static_cast<uint32_t>(i), x, f32_key(x)) ? weight(c, x) : 0.0f;
             }
+            slot_fence();
         }
     }
 }
 
-template <int DT, int NL>
-__device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, int b, const RowParams& prm, uint32_t mode,
-                           float cc, uint64_t word) {
+// The draw inside chunk cs: re-reads the chunk, weights its kept elements
+// 2^(x c - rc) * sc, finds the first element whose inclusive prefix (in
+// token order, starting at `before`) passes `target`.  Returns the token, or
+// the chunk's last kept element when rounding leaves the target unreached.
+template <int DT, int NL, typename K>
+__device__ __forceinline__ int32_t draw_in_chunk(const SampleArgs& a, FinSmem& f, int b, int cs, float cc,
+                                                 float rcs, double sc, double before, double target, K kept) {
     using G = Geo<DT, NL>;
     constexpr int VEC = G::VEC;
+    const int t = static_cast<int>(threadIdx.x), lane = lane_id(), wid = wave_id();
+    const uint32_t tbase = static_cast<uint32_t>(cs * static_cast<int>(G::ELEMS) + t * VEC);
+    u32x4_t_ d[NL];
+    load_chunk<DT, NL>(a, b, cs, d);
+    auto wt = [&](int j, int e) {
+        const float x = elem<DT>(d[j], e);
+        const uint32_t i = (tbase + j * G::SLOT + e);
+        return (x > -INFINITY && kept(i, x, f32_key(x))) ? __builtin_amdgcn_exp2f(fmaf(x, cc, -rcs)) : 0.0f;
+    };
+    // per-slot sums (fp32 per thread, fp64 across the block)
+    int my_last = -1;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float w = wt(j, e);
+            s += w;
+            if (w > 0.0f) my_last = static_cast<int>(tbase + j * G::SLOT + e);
+        }
+        const double ws = wave_sum_dpp(static_cast<double>(s));
+        if (lane == 0) f.slot[wid][j] = ws;
+        slot_fence();
+    }
+    if (t == 0) {
+        f.tok = -1;
+        f.last = -1;
+    }
+    __syncthreads();
+    if (t < NL) f.slott[t] = (f.slot[0][t] + f.slot[1][t] + f.slot[2][t] + f.slot[3][t]) * sc;
+    atomicMax(&f.last, my_last);
+    __syncthreads();
+    if (t == 0) {
+        double run = before;
+        int js = -1;
+        for (int j = 0; j < NL; ++j) {
+            if (run + f.slott[j] > target) {
+                js = j;
+                break;
+            }
+            run += f.slott[j];
+            slot_fence();
+        }
+        f.jstar = js;
+        f.before = run;
+    }
+    __syncthreads();
+    const int js = f.jstar;
+    if (js >= 0) {
+        float own = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+            if (j == js)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) own += wt(j, e);
+        uint32_t ec, tc;
+        double em, tm2;
+        block_scan2(0u, static_cast<double>(own) * sc, &ec, &em, &tc, &tm2, f);
+        const double start = f.before + em;
+        if (start <= target && start + static_cast<double>(own) * sc > target) {
+            double run = start;
+            int tok = -1;
+#pragma unroll
+            for (int j = 0; j < NL; ++j)
+                if (j == js)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        const float w = wt(j, e);
+                        run += static_cast<double>(w) * sc;
+                        if (tok < 0 && w > 0.0f && run > target) tok = static_cast<int>(tbase + j * G::SLOT + e);
+                    }
+            if (tok >= 0) f.tok = tok;
+        }
+    }
+    __syncthreads();
+    const int32_t tok = f.tok >= 0 ? f.tok : f.last;
+    __syncthreads();
+    return tok;
+}
+
+template <int DT, int NL>
+__device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, int b, const RowParams& prm,
+                                           uint32_t mode, float cc, uint64_t word) {
+    using G = Geo<DT, NL>;
     FinSmem& f = sm.f;
-    const int t = static_cast<int>(threadIdx.x), lane = lane_id();
+    const int t = static_cast<int>(threadIdx.x);
     const int S = a.chunks;
     const double u = uniform24(word);
     const SplitRec* recs = a.rec + static_cast<int64_t>(b) * a.rec_stride;
@@ -790,6 +1104,9 @@ __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, i
         f.ccnt[t] = ld_dev(&recs[t].cnt);
         f.cz[t] = ld_dev_f64(&recs[t].z);
         f.crc[t] = ld_dev_f32(&recs[t].rc);
+        f.cglo[t] = ld_dev_f32(&recs[t].glo);
+        f.cghi[t] = ld_dev_f32(&recs[t].ghi);
+        f.cwcnt[t] = ld_dev(&recs[t].wcnt);
     }
     __syncthreads();
 
@@ -811,6 +1128,7 @@ __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, i
         const float m = wave_max_dpp(mv);
         const float rref = m * cc;
         const double sc = t < S ? exp2(static_cast<double>(f.crc[t]) - static_cast<double>(rref)) : 0.0;
+        if (t < S) f.csc[t] = sc;
         const double zc = t < S ? f.cz[t] * sc : 0.0;
         const double incl = wave_scan_f64_dpp(zc);
         const double zrow = readlane_f64(incl, S - 1);
@@ -838,68 +1156,9 @@ __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, i
 
     if (mode == kModeFull) {
         const int cs = f.cstar;
-        const double sc = exp2(static_cast<double>(f.crc[cs]) - static_cast<double>(rref));
-        const double target = u * zrow;
-        // the load slot holding the target
-        if (t < kWave) {
-            const double sj = t < NL ? static_cast<double>(ld_dev_f32(&recs[cs].seg[t])) * sc : 0.0;
-            const double incl = wave_scan_f64_dpp(sj);
-            const double tb = f.before;
-            const bool past = t < NL && tb + incl > target;
-            const uint64_t bal = __ballot(past);
-            // no slot passes the target (rounding): the last slot with elements
-            int js;
-            if (bal) {
-                js = __ffsll(static_cast<long long>(bal)) - 1;
-            } else {
-                const int64_t left = a.V - static_cast<int64_t>(cs) * G::ELEMS;
-                const int64_t nslots = (left + G::SLOT - 1) / G::SLOT;
-                js = static_cast<int>((nslots < NL ? nslots : NL) - 1);
-            }
-            const double before = tb + readlane_f64(incl - sj, js);
-            if (t == 0) {
-                f.jstar = js;
-                f.before = before;
-                f.tok = -1;
-                f.last = -1;
-            }
-        }
-        __syncthreads();
-        const int js = f.jstar;
-        const double before = f.before;
-        const char* rowp = row_ptr(a, b, G::ES);
-        const int64_t sbase = static_cast<int64_t>(cs) * G::ELEMS + static_cast<int64_t>(js) * G::SLOT;
-        const uint4 v = load_slot<DT>(rowp, a.V, sbase + t * VEC);
-        const float rcs = f.crc[cs];
-        float s32 = 0.0f;
-        int my_last = -1;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const float w = __builtin_amdgcn_exp2f(fmaf(elem<DT>(v, e), cc, -rcs));
-            s32 += w;
-            if (w > 0.0f) my_last = static_cast<int>(sbase + t * VEC + e);
-        }
-        const double own = static_cast<double>(s32) * sc;
-        uint32_t ec, tc;
-        double em, tm2;
-        block_scan2(0u, own, &ec, &em, &tc, &tm2, f);
-        if (before + em <= target && before + em + own > target) {
-            double run = before + em;
-            int tok = my_last;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float w = __builtin_amdgcn_exp2f(fmaf(elem<DT>(v, e), cc, -rcs));
-                run += static_cast<double>(w) * sc;
-                if (w > 0.0f && run > target) {
-                    tok = static_cast<int>(sbase + t * VEC + e);
-                    break;
-                }
-            }
-            f.tok = tok;
-        }
-        atomicMax(&f.last, my_last);
-        __syncthreads();
-        const int32_t tok = f.tok >= 0 ? f.tok : f.last;
+        const double tok_target = u * zrow;
+        const int32_t tok = draw_in_chunk<DT, NL>(a, f, b, cs, cc, f.crc[cs], f.csc[cs], f.before, tok_target,
+                                                  [](uint32_t, float, uint32_t) { return true; });
         if (t == 0) {
             a.tokens_out[b] = tok;
             if (a.kept_out) a.kept_out[b] = a.V;
@@ -907,23 +1166,24 @@ __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, i
         }
         if (a.probs_out) {
             const double inv = 1.0 / zrow;
-            debug_probs<DT, NL>(a, b, [](int, uint32_t, uint32_t) { return true; },
+            debug_probs<DT, NL>(a, b, [](uint32_t, float, uint32_t) { return true; },
                                 [&](int c, float x) {
-                                    const double s = exp2(static_cast<double>(f.crc[c]) - static_cast<double>(rref));
                                     return static_cast<float>(
-                                        static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, cc, -f.crc[c]))) * s * inv);
+                                        static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, cc, -f.crc[c]))) *
+                                        f.csc[c] * inv);
                                 });
         }
         // the debug top-64 comes from the candidates (published with rank 64)
         if (!a.topk_idx_out) return;
     }
 
-    // ---- candidate list: every published candidate >= kappa, in token order
+    // ---- candidate list: every published candidate >= kappa, in token order.
     if (t < kWave) {
         const uint32_t cn = t < S ? f.ccnt[t] : 0u;
         const bool over = t < S && cn > static_cast<uint32_t>(kSplitCap);
-        const uint32_t incl = wave_scan_u32_dpp(over ? 0u : cn);
-        if (t < S) f.coff[t] = incl - cn;
+        const uint32_t cv = over ? 0u : cn;
+        const uint32_t incl = wave_scan_u32_dpp(cv);
+        if (t < S) f.coff[t] = incl - cv;
         const uint32_t tot = readlane_u32(incl, S - 1);
         const uint32_t kap = wave_max_u32_dpp(t < S ? f32_key(f.ctheta[t]) : 0u);
         const bool any_over = __ballot(over) != 0ull;
@@ -931,61 +1191,95 @@ __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, i
             f.coff[S] = tot;
             f.list_n = tot;
             f.kappa = kap;
-            f.bad = (any_over || tot > static_cast<uint32_t>(kListMax)) ? 1u : 0u;
+            f.bad = any_over ? 1u : 0u;
         }
     }
     __syncthreads();
-    const bool bad = f.bad != 0u;
-    const int L = bad ? 0 : static_cast<int>(f.list_n);
     const uint32_t kappa = f.kappa, maxkey = f.maxkey;
-    if (!bad) {
-        uint64_t v[8];
-        const uint64_t* cb = a.cand + static_cast<int64_t>(b) * a.rec_stride * kSplitCap;
+    bool bad = f.bad != 0u;
+    // Loads the entries of the chunk blocks (at offset `region`; per-chunk
+    // counts prefixed in f.coff, raw_n in all) that pass keep(key), in
+    // order, into the LDS list, in batches of 8 entries per thread (thread t
+    // takes 8 consecutive entries); returns how many passed.  side(chunk,
+    // key) sees every entry once.
+    auto load_list = [&](uint32_t raw_n, int region, auto keep, auto side) {
+        const uint64_t* cb = a.cand + static_cast<int64_t>(b) * a.rec_stride * kSplitCandStride + region;
+        uint32_t L32 = 0;
+        for (uint32_t batch = 0; batch < raw_n; batch += 8 * kT) {
+            uint64_t v[8];
+            int ch[8];
+            uint32_t nk = 0;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int fi = t + q * kT;
-            v[q] = 0ull;
-            if (fi < L) {
-                int lo = 0, hi = S - 1;       // the chunk c with coff[c] <= fi < coff[c + 1]
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (f.coff[mid] <= static_cast<uint32_t>(fi)) lo = mid; else hi = mid - 1;
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t fi = batch + 8 * static_cast<uint32_t>(t) + q;
+                v[q] = 0ull;
+                ch[q] = 0;
+                if (fi < raw_n) {
+                    int lo = 0, hi = S - 1;       // the chunk c with coff[c] <= fi < coff[c + 1]
+                    while (lo < hi) {
+                        const int mid = (lo + hi + 1) >> 1;
+                        if (f.coff[mid] <= fi) lo = mid; else hi = mid - 1;
+                    }
+                    ch[q] = lo;
+                    v[q] = ld_dev(cb + static_cast<int64_t>(lo) * kSplitCandStride + (fi - f.coff[lo]));
                 }
-                v[q] = ld_dev(cb + static_cast<int64_t>(lo) * kSplitCap + (fi - static_cast<int>(f.coff[lo])));
             }
-        }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int fi = t + q * kT;
-            if (fi < L) {
-                uint32_t k = static_cast<uint32_t>(v[q] >> 32);
-                const uint32_t i = static_cast<uint32_t>(v[q]);
-                if (k < kappa) k = 0u;
-                f.key[fi] = k;
-                f.idx[fi] = i;
-                f.w[fi] = k ? __builtin_amdgcn_exp2f(fmaf(key_f32(k), cc, -rref)) : 0.0f;
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t fi = batch + 8 * static_cast<uint32_t>(t) + q;
+                if (fi < raw_n) {
+                    const uint32_t k = static_cast<uint32_t>(v[q] >> 32);
+                    side(ch[q], k);
+                    nk += keep(k) ? 1u : 0u;
+                }
             }
+            uint32_t ec, tc;
+            double em, tm2;
+            block_scan2(nk, 0.0, &ec, &em, &tc, &tm2, f);
+            uint32_t pos = L32 + ec;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t fi = batch + 8 * static_cast<uint32_t>(t) + q;
+                const uint32_t k = static_cast<uint32_t>(v[q] >> 32);
+                if (fi < raw_n && keep(k)) {
+                    if (pos < static_cast<uint32_t>(kListMax)) {
+                        f.key[pos] = k;
+                        f.idx[pos] = static_cast<uint32_t>(v[q]);
+                        f.w[pos] = __builtin_amdgcn_exp2f(fmaf(key_f32(k), cc, -rref));
+                    }
+                    ++pos;
+                }
+            }
+            L32 += tc;
         }
+        __syncthreads();
+        return L32;
+    };
+    uint32_t L32 = 0;
+    if (!bad) {
+        L32 = load_list(f.list_n, 0, [&](uint32_t k) { return k >= kappa; }, [](int, uint32_t) {});
+        bad = L32 > static_cast<uint32_t>(kListMax);
     }
-    __syncthreads();
+    const int L = bad ? 0 : static_cast<int>(L32);
 
-    if (mode == kModeFull) {
-        // debug top-64 only (the token is written above)
+    if (a.topk_idx_out) {
+        const uint32_t n = prm.k < kDebugTopK ? static_cast<uint32_t>(prm.k) : static_cast<uint32_t>(kDebugTopK);
         if (!bad) {
-            debug_topk_list(a, b, f, L, kappa, maxkey,
-                            static_cast<uint32_t>(prm.k < kDebugTopK ? prm.k : kDebugTopK));
+            debug_topk_list(a, b, f, L, kappa, maxkey, n);
         } else {
             __syncthreads();
-            exact_debug_topk<DT, kT>(row_ptr(a, b, G::ES), a.V, kDebugTopK,
+            exact_debug_topk<DT, kT>(row_ptr(a, b, G::ES), a.V, static_cast<int>(n),
                                      a.topk_idx_out + static_cast<int64_t>(b) * kDebugTopK, sm.e);
+            __syncthreads();
         }
-        return;
     }
+    if (mode == kModeFull) return;
 
     // ---- top-k, then top-p inside it, then min_p
     bool ok = !bad;
     DCut cut{0u, 0xffffffffu};
     bool kp_in_list = false;
+    bool flat = false;
     const bool has_k = prm.k < a.V;
     if (ok && has_k) {
         const Found fk = descent<false>(f, L, kappa, maxkey, cut, static_cast<uint32_t>(prm.k), 0.0);
@@ -1012,6 +1306,7 @@ __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, i
             kp_in_list = true;
         } else if (!has_k) {
             kp_in_list = false;   // the nucleus reaches below kappa
+            flat = !(prm.min_p > 0.0f);
         }
     }
     if (ok && prm.min_p > 0.0f) {
@@ -1025,6 +1320,184 @@ __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, i
             kp_in_list = true;
         }
     }
+
+    if (ok && !kp_in_list && flat) {
+        // ---- flat top-p row: the boundary weight bin from the chunks' windows
+        const double target = static_cast<double>(prm.p) * zrow;
+        // the windows' common bins [GLO, GHI], the mass above every window and
+        // where each chunk's window elements start
+        if (t < kWave) {
+            const bool has = t < S;
+            const float glo = has ? f.cglo[t] : 0.0f, ghi = has ? f.cghi[t] : 0.0f;
+            const bool nowin = has && !(glo <= ghi);
+            const float GLO = -wave_min_dpp(has ? -glo : INFINITY);
+            const float GHI = wave_min_dpp(has ? ghi : INFINITY);
+            const bool usable = __ballot(nowin) == 0ull && GLO <= GHI;
+            const double am = has && usable ? ld_dev_f64(&recs[t].above_m) * f.csc[t] : 0.0;
+            const uint32_t an = has && usable ? ld_dev(&recs[t].above_n) : 0u;
+            const double AM = wave_sum_dpp(am);
+            const uint32_t AN = wave_sum_u32_dpp(an);
+            const uint32_t wc = has && usable ? f.cwcnt[t] : 0u;
+            const uint32_t wi = wave_scan_u32_dpp(wc);
+            if (has) {
+                f.coff[t] = wi - wc;
+                f.ckept[t] = am;
+            }
+            if (t == 0) {
+                f.next = usable ? 1 : 0;
+                f.list_n = readlane_u32(wi, S - 1);
+                f.amass = AM;
+                f.anum = AN;
+                f.gwlo = GLO;
+                f.gwhi = GHI;
+            }
+        }
+        for (int i = t; i < kDBins; i += kT) {
+            f.hmass[i] = 0.0;
+            f.hcnt[i] = 0u;
+        }
+        __syncthreads();
+        if (f.next) {
+            const float GLO = f.gwlo, GHI = f.gwhi;
+            const uint32_t raw_n = f.list_n;
+            // the window elements' mass by bin over [GLO, GHI] (bin GHI - q at
+            // q) and above GHI (also per chunk: it is kept whatever the cut)
+            const uint64_t* cb = a.cand + static_cast<int64_t>(b) * a.rec_stride * kSplitCandStride + kSplitCap;
+            double up = 0.0;
+            uint32_t upn = 0;
+            for (uint32_t batch = 0; batch < raw_n; batch += 8 * kT) {
+                uint64_t v[8];
+                int ch[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint32_t fi = batch + 8 * static_cast<uint32_t>(t) + q;
+                    v[q] = 0ull;
+                    ch[q] = 0;
+                    if (fi < raw_n) {
+                        int lo = 0, hi = S - 1;
+                        while (lo < hi) {
+                            const int mid = (lo + hi + 1) >> 1;
+                            if (f.coff[mid] <= fi) lo = mid; else hi = mid - 1;
+                        }
+                        ch[q] = lo;
+                        v[q] = ld_dev(cb + static_cast<int64_t>(lo) * kSplitCandStride + (fi - f.coff[lo]));
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint32_t fi = batch + 8 * static_cast<uint32_t>(t) + q;
+                    const float x = key_f32(static_cast<uint32_t>(v[q] >> 32));
+                    const float g = weight_bin(x, cc);
+                    const double w = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, cc, -rref)));
+                    if (fi < raw_n && g > GHI) {
+                        up += w;
+                        ++upn;
+                        atomicAdd(&f.ckept[ch[q]], w);
+                    } else if (fi < raw_n && g >= GLO) {
+                        const int qb = static_cast<int>(GHI - g);
+                        atomicAdd(&f.hmass[qb], w);
+                        atomicAdd(&f.hcnt[qb], 1u);
+                    }
+                }
+            }
+            uint32_t e0, upn_all;
+            double e1, up_all;
+            block_scan2(upn, up, &e0, &e1, &upn_all, &up_all, f);   // ends with a barrier
+            // D(g), the mass of the bins >= g, first reaches the target at the
+            // row's boundary bin G*, which must lie in [GLO, GHI]: D(GHI + 1) <
+            // target <= D(G*).  Thread t owns bins q = 2t, 2t + 1.
+            const double above = f.amass + up_all;
+            const uint32_t above_n = f.anum + upn_all;
+            const double h0 = f.hmass[2 * t], h1 = f.hmass[2 * t + 1];
+            const uint32_t c0 = f.hcnt[2 * t], c1 = f.hcnt[2 * t + 1];
+            uint32_t ec, tc;
+            double em, tm;
+            block_scan2(c0 + c1, h0 + h1, &ec, &em, &tc, &tm, f);
+            if (t == 0) f.next = 0;
+            __syncthreads();
+            const double base = above + em;
+            const int nb = static_cast<int>(GHI - GLO) + 1;
+            if (base < target && base + h0 >= target && 2 * t < nb) {
+                f.next = 1;
+                f.gstar = GHI - static_cast<float>(2 * t);
+                f.amass = base;
+                f.anum = above_n + ec;
+            } else if (base + h0 < target && base + h0 + h1 >= target && 2 * t + 1 < nb) {
+                f.next = 1;
+                f.gstar = GHI - static_cast<float>(2 * t + 1);
+                f.amass = base + h0;
+                f.anum = above_n + ec + c0;
+            }
+            __syncthreads();
+        }
+        if (f.next) {
+            const float gstar = f.gstar, GHI = f.gwhi;
+            const double A = f.amass;
+            const uint32_t N = f.anum;
+            // the boundary bin's elements, from the windows; the windows' mass in
+            // (G*, GHI] joins the kept mass of its chunk
+            const uint32_t Lw = load_list(
+                f.list_n, kSplitCap, [&](uint32_t k) { return weight_bin(key_f32(k), cc) == gstar; },
+                [&](int c, uint32_t k) {
+                    const float x = key_f32(k);
+                    const float g = weight_bin(x, cc);
+                    if (g > gstar && g <= GHI)
+                        atomicAdd(&f.ckept[c], static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, cc, -rref))));
+                });
+            if (Lw <= static_cast<uint32_t>(kListMax)) {
+                const int Lb = static_cast<int>(Lw);
+                const Found fb = descent<true>(f, Lb, 1u, maxkey, DCut{0u, 0xffffffffu}, 0u, target, N, A);
+                if (fb.ok) {
+                    const DCut bc = fb.cut;
+                    // kept bin-G* mass per chunk
+                    for (int i = t; i < Lb; i += kT) {
+                        if (kept_by(bc, f.key[i], f.idx[i]))
+                            atomicAdd(&f.ckept[f.idx[i] / G::ELEMS], static_cast<double>(f.w[i]));
+                    }
+                    __syncthreads();
+                    if (t < kWave) {
+                        const double kc = t < S ? f.ckept[t] : 0.0;
+                        const double incl = wave_scan_f64_dpp(kc);
+                        const double W = readlane_f64(incl, S - 1);
+                        const double tgt = u * W;
+                        const uint64_t bal = __ballot(t < S && incl > tgt);
+                        const int cs = bal ? __ffsll(static_cast<long long>(bal)) - 1 : S - 1;
+                        const double before = readlane_f64(incl - kc, cs);
+                        if (t == 0) {
+                            f.cstar = cs;
+                            f.before = before;
+                            f.zrow = W;   // kept mass (relative to rref)
+                        }
+                    }
+                    __syncthreads();
+                    const int cs = f.cstar;
+                    const double W = f.zrow;
+                    auto keptf = [&](uint32_t i, float x, uint32_t k) {
+                        const float g = weight_bin(x, cc);
+                        return g > gstar || (g == gstar && kept_by(bc, k, i));
+                    };
+                    const int32_t tok = draw_in_chunk<DT, NL>(a, f, b, cs, cc, f.crc[cs], f.csc[cs], f.before,
+                                                              u * W, keptf);
+                    if (t == 0) {
+                        a.tokens_out[b] = tok;
+                        if (a.kept_out) a.kept_out[b] = static_cast<int32_t>(fb.n);
+                        if (a.rand_out) a.rand_out[b] = word;
+                    }
+                    if (a.probs_out) {
+                        const double inv = 1.0 / W;
+                        debug_probs<DT, NL>(a, b, keptf, [&](int c, float x) {
+                            return static_cast<float>(
+                                static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, cc, -f.crc[c]))) * f.csc[c] *
+                                inv);
+                        });
+                    }
+                    return;
+                }
+            }
+        }
+        ok = false;
+    }
+
     ok = ok && kp_in_list;
     if (!ok) {
         __syncthreads();
@@ -1081,39 +1554,41 @@ __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, i
         const double inv = 1.0 / W;
         const DCut fc = cut;
         debug_probs<DT, NL>(a, b,
-                            [&](int, uint32_t i, uint32_t k) { return k >= kappa && kept_by(fc, k, i); },
+                            [&](uint32_t i, float, uint32_t k) { return k >= kappa && kept_by(fc, k, i); },
                             [&](int, float x) {
                                 return static_cast<float>(
                                     static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, cc, -rref))) * inv);
                             });
     }
-    if (a.topk_idx_out) {
-        __syncthreads();
-        const uint32_t n = prm.k < kDebugTopK ? static_cast<uint32_t>(prm.k) : static_cast<uint32_t>(kDebugTopK);
-        debug_topk_list(a, b, f, L, kappa, maxkey, n);
-    }
 }
 
 template <int DT, int NL>
-__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4, 8))) void sample_split_kernel(SampleArgs a) {
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(DST_SPLIT_WAVES_PER_EU, 8)))
+void sample_split_kernel(SampleArgs a) {
     __shared__ SplitSmem sm;
     const int S = a.chunks;
     // workgroup -> (row, chunk): XCD x = blockIdx mod 8 takes rows x, x + 8, ...;
     // a row's chunks are consecutive on its XCD, chunk S - 1 last
+    // (readfirstlane: the compiler cannot see through the division that
+    // these are wave-uniform, and a row pointer in vector registers would
+    // turn every buffer load into a loop over lanes)
     const int x = static_cast<int>(blockIdx.x) & (kSplitXcds - 1);
     const int kk = static_cast<int>(blockIdx.x) / kSplitXcds;
-    const int rl = kk / S;
-    const int c_own = kk - rl * S;
-    const int b = rl * kSplitXcds + x;
+    const int rl = __builtin_amdgcn_readfirstlane(kk / S);
+    const int c_own = __builtin_amdgcn_readfirstlane(kk - rl * S);
+    const int b = __builtin_amdgcn_readfirstlane(rl * kSplitXcds + x);
     if (b >= a.B) return;
     const bool finisher = c_own == S - 1;
 
     const RowParams prm = row_params(a.temperature, a.top_k, a.top_p, a.min_p, b, a.V);
     const bool dbg_list = a.topk_idx_out != nullptr;
+    // top-p rows aim at about kPList candidates over the whole row
+    const int jtopp = kPList / S < kJMax ? (kPList / S > 1 ? kPList / S : 1) : kJMax;
     // route; candidate rank aimed at (scaled by the chunk's length) and the
     // rank every chunk must cover whatever its length
     uint32_t mode;
     int jrank = 0, jmin = 0;
+    float flat_p = 0.0f;
     if (prm.greedy || prm.k == 1) {
         mode = kModeArgmax;
     } else if (prm.k < a.V && prm.k <= kKList) {
@@ -1121,12 +1596,13 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
         jrank = jmin = prm.k;
     } else if (prm.k < a.V) {
         mode = prm.k <= kJMax ? kModeTopP : kModeExact;
-        jrank = kJTopP;
+        jrank = jtopp;
         jmin = prm.k;
     } else if (prm.top_p || prm.min_p > 0.0f) {
         mode = kModeTopP;
-        jrank = kJTopP;
+        jrank = jtopp;
         jmin = dbg_list ? kJDebug : 1;
+        flat_p = prm.top_p && !(prm.min_p > 0.0f) ? prm.p : 0.0f;
     } else {
         mode = kModeFull;
         jrank = jmin = dbg_list ? kJDebug : 0;
@@ -1141,7 +1617,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
         return;
     }
 
-    chunk_phase<DT, NL>(a, sm.c, b, c_own, mode, cc, jrank, jmin);
+    chunk_phase<DT, NL>(a, sm.c, b, c_own, mode, cc, jrank, jmin, flat_p);
     wait_all_memory();
     __syncthreads();
     if (!finisher) {
@@ -1176,16 +1652,11 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     finish_row<DT, NL>(a, sm, b, prm, mode, cc, word);
 }
 
-template <int DT>
-hipError_t launch_dt(const SampleArgs& args, int nl, hipStream_t stream) {
+template <int DT, int NL>
+hipError_t launch_nl(const SampleArgs& args, hipStream_t stream) {
     const int rows_per_xcd = (args.B + kSplitXcds - 1) / kSplitXcds;
     const dim3 grid(static_cast<unsigned>(kSplitXcds * rows_per_xcd * args.chunks));
-    if (nl == 4)
-        hipLaunchKernelGGL((sample_split_kernel<DT, 4>), grid, dim3(kT), 0, stream, args);
-    else if (DT == kDtypeF32 && nl == 8)
-        hipLaunchKernelGGL((sample_split_kernel<kDtypeF32, 8>), grid, dim3(kT), 0, stream, args);
-    else
-        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((sample_split_kernel<DT, NL>), grid, dim3(kT), 0, stream, args);
     return hipGetLastError();
 }
 
@@ -1197,11 +1668,10 @@ int split_plan(int V, int dtype, int* chunks) {
         const int64_t e = static_cast<int64_t>(kSplitThreads) * nl * vec;
         return static_cast<int64_t>((V + e - 1) / e);
     };
-    // Eight 16-byte loads per thread at most for fp32 rows and four for bf16
-    // rows: the chunk and the compaction state then fit in 128 VGPRs (four
-    // waves per SIMD) with no scratch.  fp32 rows take eight unless that
-    // leaves fewer than eight chunks per row.
-    const int nl = (dtype == kDtypeF32 && nchunks(8) >= 8) ? 8 : 4;
+    // the large chunk unless that leaves fewer than four chunks per row (short
+    // rows fill the GPU with more, smaller chunks)
+    const int big = dtype == kDtypeF32 ? DST_SPLIT_NL_F32 : DST_SPLIT_NL_BF16;
+    const int nl = nchunks(big) >= 4 ? big : 4;
     if (V < 1 || nchunks(nl) > kSplitMaxChunks) return 0;
     *chunks = static_cast<int>(nchunks(nl));
     return nl;
@@ -1214,7 +1684,14 @@ int split_chunks_alloc(int V, int dtype) {
 
 hipError_t launch_sample_split(const SampleArgs& args, int dtype, int nl, hipStream_t stream) {
     if (args.chunks < 1 || args.chunks > kSplitMaxChunks || args.chunks > args.rec_stride) return hipErrorInvalidValue;
-    return dtype == kDtypeF32 ? launch_dt<kDtypeF32>(args, nl, stream) : launch_dt<kDtypeBF16>(args, nl, stream);
+    if (dtype == kDtypeF32) {
+        if (nl == 4) return launch_nl<kDtypeF32, 4>(args, stream);
+        if (nl == DST_SPLIT_NL_F32) return launch_nl<kDtypeF32, DST_SPLIT_NL_F32>(args, stream);
+    } else {
+        if (nl == 4) return launch_nl<kDtypeBF16, 4>(args, stream);
+        if (nl == DST_SPLIT_NL_BF16) return launch_nl<kDtypeBF16, DST_SPLIT_NL_BF16>(args, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace dst

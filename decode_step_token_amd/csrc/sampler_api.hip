@@ -161,7 +161,7 @@ int sampler_create(dst_sampler** out, int device, int32_t max_batch, int32_t voc
     const size_t rows = static_cast<size_t>(max_batch);
     const size_t nrec = rows * static_cast<size_t>(s->split_nl ? s->split_chunks : 0);
     const size_t rec_bytes = nrec * sizeof(dst::SplitRec);
-    const size_t cand_bytes = nrec * dst::kSplitCap * sizeof(uint64_t);
+    const size_t cand_bytes = nrec * dst::kSplitCandStride * sizeof(uint64_t);
     const size_t flag_bytes = rows * dst::kSplitMaxChunks * sizeof(uint32_t);
     hipError_t e = hipSuccess;
     if (s->split_nl) {
