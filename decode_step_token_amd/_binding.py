@@ -23,6 +23,8 @@ SAMPLER_F32 = 0
 SAMPLER_BF16 = 1
 SAMPLER_DEBUG_TOPK = 64
 SAMPLER_DEBUG_FORCE_EXACT = 1
+SAMPLER_DEBUG_FORCE_STREAM = 2
+SAMPLER_DEBUG_FORCE_SPLIT = 4
 
 STATUS = {0: "SAMPLER_OK", -1: "SAMPLER_EINVAL", -2: "SAMPLER_ENOMEM", -3: "SAMPLER_EHIP",
           -4: "SAMPLER_ENOTPINNED", -5: "SAMPLER_EDEVICE", -6: "SAMPLER_ETICKET"}
@@ -160,7 +162,9 @@ def sample_batch(handle, logits: torch.Tensor, temperature=None, top_k=None, top
                           ("topk_idx_out", torch.int32), ("rand_out", torch.int64)):
             t = debug.get(field)
             setattr(dbg, field, None if t is None else _ptr(t, field, dt, None, dev).value)
-        dbg.flags = SAMPLER_DEBUG_FORCE_EXACT if debug.get("force_exact") else 0
+        dbg.flags = ((SAMPLER_DEBUG_FORCE_EXACT if debug.get("force_exact") else 0)
+                     | (SAMPLER_DEBUG_FORCE_STREAM if debug.get("force_stream") else 0)
+                     | (SAMPLER_DEBUG_FORCE_SPLIT if debug.get("force_split") else 0))
     code = load().sample_batch(
         handle, _stream(stream), ctypes.c_void_p(logits.data_ptr()), stride, B,
         _ptr(temperature, "temperature", torch.float32, B, dev),

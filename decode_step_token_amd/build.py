@@ -19,8 +19,8 @@ BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdst_sampler.so")
 
-SOURCES = ["sample_split.hip", "sample_exact.hip", "write_tokens.hip",
-           "prepare.hip", "page_table.hip", "sampler_api.hip"]
+SOURCES = ["sample_stream.hip", "sample_split.hip", "sample_exact.hip", "argmax.hip",
+           "write_tokens.hip", "prepare.hip", "page_table.hip", "sampler_api.hip"]
 HEADERS = ["device_common.hpp", "kernels.hpp", "exact_path.hpp"]
 
 ARCH = "gfx950"

@@ -32,20 +32,22 @@ struct SplitRec {
     double z;          // sum of the chunk's weights 2^(x c - rc)
     float rc;          // fl(m * c): the weights' reference
     uint32_t mode;
-    // window of weight bins around the chunk's own top-p boundary (flat
-    // top-p chunks only; glo > ghi: none).  Bins are floor(16 x c), absolute.
-    float glo, ghi;
-    uint32_t wcnt;     // window elements published (after the candidates)
-    uint32_t above_n;  // elements in bins above ghi
-    double above_m;    // their weight (relative to rc)
-    uint32_t pad[18];
+    // second publication of rows without a top-k filter, once the row's
+    // boundary weight bin G* and min_p key are known
+    double am_all;     // weight of the elements in bins above G*
+    double am_kept;    // ... of those whose key passes min_p
+    uint32_t an_all;   // their counts
+    uint32_t an_kept;
+    uint32_t bcnt;     // elements of bin G* published (after the candidates)
+    uint32_t pad[17];
 };
 static_assert(sizeof(SplitRec) == 128, "record size");
 
 constexpr int kSplitThreads = 256;
 constexpr int kSplitCap = 256;        // candidates one chunk may publish
-constexpr int kSplitWinCap = 1024;    // window elements one chunk may publish
-constexpr int kSplitCandStride = kSplitCap + kSplitWinCap;   // entries per chunk block
+constexpr int kSplitBinCap = 1024;    // elements of bin G* one chunk may publish
+constexpr int kSplitCandStride = kSplitCap + kSplitBinCap;   // entries per chunk block
+constexpr int kSplitHistBins = 1024;  // weight histogram per chunk: 1/32 octave per bin
 constexpr int kSplitMaxChunks = 64;   // chunks per row (one flag per lane of a wave)
 constexpr int kSplitXcds = 8;         // rows are dealt to the XCDs round robin
 
@@ -68,10 +70,13 @@ struct SampleArgs {
     // split-row sampler workspace (see SplitRec)
     SplitRec* rec;             // [B][rec_stride]
     uint64_t* cand;            // [B][rec_stride][kSplitCandStride] (order key << 32 | index)
+    float* hist;               // [B][rec_stride][kSplitHistBins]
+    uint32_t* dec;             // [B][4] the finisher's decision: epoch, G*, min_p key, status
     uint32_t* flags;           // [B][kSplitMaxChunks] epoch of the last publication
     int rec_stride;            // chunks allocated per row
     int chunks;                // chunks per row in this launch
-    uint32_t epoch;            // nonzero, different for every launch on a workspace
+    uint32_t epoch;            // even, nonzero, different for every launch on a workspace;
+                               // the second publication of a launch is flagged epoch + 1
 };
 
 struct WriteArgs {

@@ -39,24 +39,27 @@
 // holds every element of the row at or above kappa = the largest chunk
 // threshold.
 //
-// Flat top-p rows (a nucleus deeper than the candidates: high temperature or
-// logits without a dominant head).  A top-p chunk whose candidates hold less
-// than p of its own mass also histograms its weights in bins of 1/16 octave
-// (floor(16 x log2(e) / T), a grid common to every chunk of the row), finds
-// the bin where its own descending mass reaches p, and publishes the
-// elements of a window of bins around it (grown while it holds at most about
-// 768 elements, so narrow where the row is dense) with the mass and count of
-// everything above the window.  The row's boundary bin lies between the
-// smallest and the largest of the chunks' own boundary bins; when it lies in
-// every chunk's window, the finisher locates it from the published elements
-// and masses and resolves the cut inside it.
+// Rows without a top-k filter (top-p and / or min_p).  Their nucleus can hold
+// tens of thousands of tokens, far more than any candidate list, so they are
+// cut through a weight histogram instead.  Every chunk of such a row also
+// adds its weights into bins of 1/32 octave on a grid common to the whole row
+// (floor(32 x log2(e) / T)) and publishes that histogram with its record.
+// The finisher sums the chunks' histograms, finds the bin G* where the
+// descending mass first reaches p of the row's (and the min_p key from the
+// row maximum) and publishes that decision; the chunks, still holding their
+// elements in registers, then publish the weight and count of everything
+// above bin G* and the elements of bin G* itself in token order, and the
+// finisher resolves the cut inside bin G* exactly.  The chunks of such a row
+// wait for their finisher, which is dispatched after them on the same XCD:
+// every earlier row's finisher is already resident, so the wait always ends
+// (and it is bounded all the same).
 //
 // The finisher loads the candidates >= kappa into LDS (in token order) and
 // finds cuts by descents over key histograms (by count for top-k, by mass
 // for top-p), resolving the boundary bin exactly.  Rows whose kept set is in
 // the list draw by a block-wide scan of the kept weights in token order;
-// rows with no filter and flat rows find the chunk holding the target from
-// the published masses and re-read that one chunk.  Whatever the published
+// rows with no filter and rows cut through the histogram find the chunk
+// holding the target from the published masses and re-read that one chunk.  Whatever the published
 // data cannot settle is finished by the exact multi-pass routine over the
 // whole row.
 #include "device_common.hpp"
@@ -64,13 +67,13 @@
 #include "kernels.hpp"
 
 #ifndef DST_SPLIT_NL_F32
-#define DST_SPLIT_NL_F32 16     // 16-byte loads per thread and chunk, fp32 rows
+#define DST_SPLIT_NL_F32 8      // 16-byte loads per thread and chunk, fp32 rows
 #endif
 #ifndef DST_SPLIT_NL_BF16
-#define DST_SPLIT_NL_BF16 16    // ... bf16 rows
+#define DST_SPLIT_NL_BF16 8     // ... bf16 rows
 #endif
 #ifndef DST_SPLIT_WAVES_PER_EU
-#define DST_SPLIT_WAVES_PER_EU 5
+#define DST_SPLIT_WAVES_PER_EU 4
 #endif
 
 namespace dst {
@@ -81,26 +84,27 @@ constexpr int kT = kSplitThreads;
 constexpr int kNW = kT / kWave;
 constexpr int kGBins = 1024;          // group-maximum histogram: 1/16 logit per bin
 constexpr int kDBins = 512;           // descent histograms
-constexpr int kHBins = 512;           // flat chunks: weight histogram, 1/16 octave per bin
-constexpr int kWinBudget = 768;       // elements a flat chunk's window aims to hold
+constexpr int kWBins = kSplitHistBins;   // weight histogram: 1/32 octave per bin
 constexpr int kListMax = 1536;        // candidates the finisher holds
 constexpr int kKList = 128;           // top-k rows up to this k aim their thresholds at k
 constexpr int kPList = 1200;          // top-p / min_p rows: candidates aimed at per row
 constexpr int kJMax = 224;            // largest rank aimed at (a chunk publishes <= kSplitCap)
 constexpr int kJDebug = 64;           // debug: the row's 64 largest
 constexpr float kGroupBinScale = 16.0f;
-constexpr float kWeightBinScale = 16.0f;
+constexpr float kWeightBinScale = 32.0f;
 constexpr int kSpinLimit = 1 << 16;
 constexpr int kSmall = 64;
 
-enum : uint32_t { kModeArgmax = 0, kModeTopK = 1, kModeTopP = 2, kModeFull = 3, kModeExact = 4 };
+// kModeTopP: a top-k filter above kKList (cut through the candidates);
+// kModeHist: top-p and / or min_p without a top-k filter (cut through the
+// weight histogram)
+enum : uint32_t { kModeArgmax = 0, kModeTopK = 1, kModeTopP = 2, kModeFull = 3, kModeExact = 4, kModeHist = 5 };
 
 static_assert(kT == 256 && kNW == 4, "the block layout below assumes 4 waves");
 
 struct ChunkSmem {
     uint32_t gh[kGBins];
-    float wh[kHBins];
-    uint32_t wcn[kHBins];
+    double wh[kWBins];
     uint32_t wtot[kNW][16];
     uint32_t off[kNW][16];
     double dred[kNW][8];
@@ -108,7 +112,6 @@ struct ChunkSmem {
     float fred[kNW];
     uint64_t ured[kNW];
     uint32_t bsel, total;
-    int rsel, rlo, rhi;
 };
 
 struct FinSmem {
@@ -124,9 +127,7 @@ struct FinSmem {
     double cz[kSplitMaxChunks];
     float crc[kSplitMaxChunks];
     double csc[kSplitMaxChunks];       // 2^(rc_c - rref)
-    float cglo[kSplitMaxChunks], cghi[kSplitMaxChunks];
-    uint32_t cwcnt[kSplitMaxChunks];
-    double ckept[kSplitMaxChunks];     // flat rows: kept mass per chunk
+    double ckept[kSplitMaxChunks];     // histogram rows: kept mass per chunk
     uint32_t coff[kSplitMaxChunks + 1];
     uint32_t skey[kSmall];
     uint32_t sidx[kSmall];
@@ -147,7 +148,7 @@ struct FinSmem {
     uint32_t list_n, kappa, maxkey, bad;
     double zrow, before, amass;
     uint32_t anum;
-    float gstar, gwlo, gwhi;
+    float gstar;
     int cstar, jstar, next;
 };
 
@@ -181,6 +182,31 @@ __device__ __forceinline__ void st_dev_f64(double* p, double v) {
 __device__ __forceinline__ double ld_dev_f64(const double* p) {
     return __longlong_as_double(static_cast<long long>(ld_dev(reinterpret_cast<const uint64_t*>(p))));
 }
+
+// Bulk reads of data published earlier in this launch (after its flag was
+// seen): buffer loads with the sc1 cache policy, which read the L2 the
+// publishing stores wrote through to, never a stale L1 line.  Plain loads,
+// unlike the atomic ones above, so the compiler issues a batch before
+// waiting; offsets past the buffer's size read 0 (kL2None).
+constexpr int kSc1 = 16;
+constexpr uint32_t kL2None = 0x7ffffff0u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t l2_rsrc(const void* base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(nbytes), 0x00020000);
+}
+__device__ __forceinline__ uint32_t l2_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSc1);
+}
+__device__ __forceinline__ float l2_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) { return __uint_as_float(l2_u32(r, off)); }
+__device__ __forceinline__ uint64_t l2_u64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSc1);
+    return static_cast<uint64_t>(v[0]) | (static_cast<uint64_t>(v[1]) << 32);
+}
+__device__ __forceinline__ double l2_f64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __longlong_as_double(static_cast<long long>(l2_u64(r, off)));
+}
+// byte offset of a record field
+#define DST_REC_OFF(c, field) (static_cast<uint32_t>(c) * static_cast<uint32_t>(sizeof(SplitRec)) + \
+                               static_cast<uint32_t>(offsetof(SplitRec, field)))
 
 // Waits until every memory operation this thread issued has completed.
 __device__ __forceinline__ void wait_all_memory() {
@@ -346,7 +372,7 @@ __device__ __forceinline__ void load_chunk(const SampleArgs& a, int b, int c, u3
     }
 }
 
-// The common weight-bin grid of a row: floor(16 x log2(e) / T).
+// The common weight-bin grid of a row: floor(32 x log2(e) / T).
 __device__ __forceinline__ float weight_bin(float x, float cc) {
     return floorf(x * cc * kWeightBinScale);
 }
@@ -367,11 +393,6 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, ChunkSmem& sm, int
     return sm.ured32[0][slot] + sm.ured32[1][slot] + sm.ured32[2][slot] + sm.ured32[3][slot];
 }
 
-// The chunk's part of the row: loads it, reduces it and publishes its record
-// and candidates (see the file comment).  mode is the row's route, cc the
-// fp32 log2(e)/T, jrank the candidate rank target scaled by the chunk's
-// length, jmin the rank every chunk covers; flat_p > 0 enables the window of
-// flat top-p chunks (the row's top-p).
 // Ordered compaction: the chunk's elements that pass keep(x), in token order
 // (per slot, those of lower threads first; slot counts travel two to a
 // register through the wave scan), written as (order key << 32 | index) to
@@ -437,16 +458,18 @@ __device__ __forceinline__ uint32_t ordered_publish(u32x4_t_ (&d)[NL], ChunkSmem
     return total;
 }
 
+// The first publication of a chunk (held in d): its record, its candidates
+// when jrank > 0 (the rank aimed at, scaled by the chunk's length; jmin the
+// rank every chunk covers), and its weight histogram when whist.  mode is
+// the row's route, cc the fp32 log2(e)/T.  Returns rc.
 template <int DT, int NL>
-__device__ __forceinline__ void chunk_phase(const SampleArgs& a, ChunkSmem& sm, int b, int c, uint32_t mode,
-                                            float cc, int jrank, int jmin, float flat_p) {
+__device__ __forceinline__ float chunk_phase(const SampleArgs& a, ChunkSmem& sm, int b, int c, u32x4_t_ (&d)[NL],
+                                             uint32_t mode, float cc, int jrank, int jmin, bool whist) {
     using G = Geo<DT, NL>;
     constexpr int VEC = G::VEC;
     const int t = static_cast<int>(threadIdx.x), lane = lane_id(), wid = wave_id();
     const int base = c * static_cast<int>(G::ELEMS);
     const uint32_t tbase = static_cast<uint32_t>(base + t * VEC);
-    u32x4_t_ d[NL];
-    load_chunk<DT, NL>(a, b, c, d);
 
     SplitRec* rec = a.rec + static_cast<int64_t>(b) * a.rec_stride + c;
 
@@ -481,7 +504,7 @@ __device__ __forceinline__ void chunk_phase(const SampleArgs& a, ChunkSmem& sm, 
             st_dev(&rec->cnt, 0u);
             st_dev(&rec->mode, mode);
         }
-        return;
+        return 0.0f;
     }
 
     // group (16-byte load) maxima, recomputed where needed rather than held
@@ -491,6 +514,10 @@ __device__ __forceinline__ void chunk_phase(const SampleArgs& a, ChunkSmem& sm, 
         for (int e = 1; e < VEC; ++e) g = fmaxf(g, elem<DT>(d[j], e));
         return g;
     };
+    if (whist) {
+#pragma unroll
+        for (int q = 0; q < kWBins / kT; ++q) sm.wh[q * kT + t] = 0.0;
+    }
     float tm = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NL; ++j) tm = fmaxf(tm, group_max(j));
@@ -501,27 +528,38 @@ __device__ __forceinline__ void chunk_phase(const SampleArgs& a, ChunkSmem& sm, 
     const float mc = fmaxf(fmaxf(sm.fred[0], sm.fred[1]), fmaxf(sm.fred[2], sm.fred[3]));
 
     // softmax weights 2^(x c - rc): fp32 over the thread's elements, fp64
-    // across the block
-    const float rc = mc * cc;
+    // across the block; with whist also by weight bin below the chunk's top
+    // bin (fp64 in LDS, the deepest bin holding everything below)
+    const float rc = mc > -INFINITY ? mc * cc : 0.0f;   // a chunk of -inf only: every weight 0
     double z = 0.0;
-    if (mode == kModeTopP || mode == kModeFull) {
+    if (mode == kModeTopP || mode == kModeFull || mode == kModeHist) {
+        const float gtop = weight_bin(mc, cc);
         float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const float w = __builtin_amdgcn_exp2f(fmaf(elem<DT>(d[j], e), cc, -rc));
+                const float x = elem<DT>(d[j], e);
+                const float w = __builtin_amdgcn_exp2f(fmaf(x, cc, -rc));
                 if (e & 1) s1 += w; else s0 += w;
+                if (whist && x > -INFINITY) {
+                    const int r = static_cast<int>(fminf(gtop - weight_bin(x, cc), kWBins - 1.0f));
+                    atomicAdd(&sm.wh[r], static_cast<double>(w));
+                }
             }
             slot_fence();
         }
         opaque(d);
-        z = block_sum_f64(static_cast<double>(s0) + static_cast<double>(s1), sm, 0);
+        z = block_sum_f64(static_cast<double>(s0) + static_cast<double>(s1), sm, 0);   // also orders the histogram
+        if (whist) {
+            float* ho = a.hist + (static_cast<int64_t>(b) * a.rec_stride + c) * kWBins;
+#pragma unroll
+            for (int q = 0; q < kWBins / kT; ++q) st_dev_f32(ho + q * kT + t, static_cast<float>(sm.wh[q * kT + t]));
+        }
     }
 
     float theta = INFINITY;
     uint32_t total = 0;
-    double cand_mass = 0.0;
     if (jrank > 0) {
         const int64_t valid = a.V - base < G::ELEMS ? a.V - base : G::ELEMS;   // elements in the chunk
         const int64_t scaled = (static_cast<int64_t>(jrank) * valid + G::ELEMS - 1) / G::ELEMS;
@@ -597,117 +635,10 @@ __device__ __forceinline__ void chunk_phase(const SampleArgs& a, ChunkSmem& sm, 
         __syncthreads();
         theta = fminf(fminf(sm.fred[0], sm.fred[1]), fminf(sm.fred[2], sm.fred[3]));
 
-        float cm32 = 0.0f;
-        total = ordered_publish<DT, NL>(
-            d, sm, tbase, a.cand + (static_cast<int64_t>(b) * a.rec_stride + c) * kSplitCandStride,
-            static_cast<uint32_t>(kSplitCap), [&](float x) { return x >= theta; },
-            [&](float x) { cm32 += __builtin_amdgcn_exp2f(fmaf(x, cc, -rc)); });
-        if (flat_p > 0.0f) cand_mass = block_sum_f64(static_cast<double>(cm32), sm, 1);
-    }
-
-    // flat top-p chunk: the window of weight bins around its own boundary
-    float glo = 1.0f, ghi = 0.0f;
-    if (flat_p > 0.0f && total <= static_cast<uint32_t>(kSplitCap) && cand_mass < static_cast<double>(flat_p) * z) {
-        for (int i = t; i < kHBins; i += kT) {
-            sm.wh[i] = 0.0f;
-            sm.wcn[i] = 0u;
-        }
-        if (t == 0) sm.rsel = -1;
-        __syncthreads();
-        const float gtop = weight_bin(mc, cc);
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float x = elem<DT>(d[j], e);
-                if (x > -INFINITY) {
-                    const int r = static_cast<int>(fminf(gtop - weight_bin(x, cc), kHBins - 1.0f));
-                    atomicAdd(&sm.wh[r], __builtin_amdgcn_exp2f(fmaf(x, cc, -rc)));
-                    atomicAdd(&sm.wcn[r], 1u);
-                }
-            }
-            slot_fence();
-        }
-        opaque(d);
-        __syncthreads();
-        // the bin where the descending mass reaches flat_p of the chunk's
-        // (thread t owns bins 2t, 2t + 1)
-        const double target = static_cast<double>(flat_p) * z;
-        const double h0 = sm.wh[2 * t], h1 = sm.wh[2 * t + 1];
-        const double inc = wave_scan_f64_dpp(h0 + h1);
-        if (lane == kWave - 1) sm.dred[wid][2] = inc;
-        __syncthreads();
-        double ex = inc - (h0 + h1);
-#pragma unroll
-        for (int w = 0; w < kNW; ++w) ex += w < wid ? sm.dred[w][2] : 0.0;
-        if (ex < target && ex + h0 >= target) sm.rsel = 2 * t;
-        else if (ex + h0 < target && ex + h0 + h1 >= target) sm.rsel = 2 * t + 1;
-        __syncthreads();
-        if (t == 0) {
-            // grow the window from that bin, one bin up and one down in turn,
-            // while it holds at most kWinBudget elements; the deepest bin (all
-            // the deeper weights) never belongs to it
-            const int rs = sm.rsel;
-            int lo = rs, hi = rs;
-            uint32_t cnt = rs >= 0 ? sm.wcn[rs] : 0u;
-            bool up = true, down = true;
-            while (rs >= 0 && (up || down)) {
-                if (up) {
-                    up = lo > 0 && cnt + sm.wcn[lo - 1] <= static_cast<uint32_t>(kWinBudget);
-                    if (up) cnt += sm.wcn[--lo];
-                }
-                if (down) {
-                    down = hi + 1 < kHBins - 1 && cnt + sm.wcn[hi + 1] <= static_cast<uint32_t>(kWinBudget);
-                    if (down) cnt += sm.wcn[++hi];
-                }
-            }
-            const bool usable = rs >= 0 && hi < kHBins - 1 && cnt <= static_cast<uint32_t>(kSplitWinCap);
-            sm.rlo = usable ? lo : -1;
-            sm.rhi = hi;
-        }
-        __syncthreads();
-        if (sm.rlo >= 0) {
-            glo = gtop - static_cast<float>(sm.rhi);
-            ghi = gtop - static_cast<float>(sm.rlo);
-            // everything above the window: its mass and count
-            float am = 0.0f;
-            uint32_t an = 0;
-#pragma unroll
-            for (int j = 0; j < NL; ++j) {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const float x = elem<DT>(d[j], e);
-                    if (x > -INFINITY && weight_bin(x, cc) > ghi) {
-                        am += __builtin_amdgcn_exp2f(fmaf(x, cc, -rc));
-                        ++an;
-                    }
-                }
-                slot_fence();
-            }
-            opaque(d);
-            const double am_b = block_sum_f64(static_cast<double>(am), sm, 3);
-            const uint32_t an_b = block_sum_u32(an, sm, 0);
-            // the window's elements, in token order (their masses are derived
-            // by the finisher)
-            const float wlo = glo, whi = ghi;
-            const uint32_t wn = ordered_publish<DT, NL>(
-                d, sm, tbase,
-                a.cand + (static_cast<int64_t>(b) * a.rec_stride + c) * kSplitCandStride + kSplitCap,
-                static_cast<uint32_t>(kSplitWinCap),
-                [&](float x) {
-                    const float g = weight_bin(x, cc);
-                    return x > -INFINITY && g >= wlo && g <= whi;
-                },
-                [](float) {});
-            if (wn > static_cast<uint32_t>(kSplitWinCap)) {
-                glo = 1.0f;
-                ghi = 0.0f;
-            } else if (t == 0) {
-                st_dev(&rec->wcnt, wn);
-                st_dev_f64(&rec->above_m, am_b);
-                st_dev(&rec->above_n, an_b);
-            }
-        }
+        total = ordered_publish<DT, NL>(d, sm, tbase,
+                                       a.cand + (static_cast<int64_t>(b) * a.rec_stride + c) * kSplitCandStride,
+                                       static_cast<uint32_t>(kSplitCap), [&](float x) { return x >= theta; },
+                                       [](float) {});
     }
 
     if (t == 0) {
@@ -718,8 +649,59 @@ __device__ __forceinline__ void chunk_phase(const SampleArgs& a, ChunkSmem& sm, 
         st_dev(&rec->cnt, jrank > 0 ? (total <= static_cast<uint32_t>(kSplitCap) ? total : kSplitCap + 1u) : 0u);
         st_dev_f32(&rec->rc, rc);
         st_dev(&rec->mode, mode);
-        st_dev_f32(&rec->glo, glo);
-        st_dev_f32(&rec->ghi, ghi);
+    }
+    return rc;
+}
+
+// The second publication of a histogram row's chunk, once the finisher has
+// decided the boundary bin gstar (-inf: min_p alone) and the min_p key kmin
+// (0: none): the weight and count of the elements in bins above gstar, all
+// and those with key >= kmin, and (when bin) the elements of bin gstar in
+// token order.
+template <int DT, int NL>
+__device__ __forceinline__ void hist_phase2(const SampleArgs& a, ChunkSmem& sm, int b, int c, u32x4_t_ (&d)[NL],
+                                            float cc, float rc, float gstar, uint32_t kmin, bool bin) {
+    using G = Geo<DT, NL>;
+    constexpr int VEC = G::VEC;
+    const int t = static_cast<int>(threadIdx.x);
+    const uint32_t tbase = static_cast<uint32_t>(c * static_cast<int>(G::ELEMS) + t * VEC);
+    SplitRec* rec = a.rec + static_cast<int64_t>(b) * a.rec_stride + c;
+    float am = 0.0f, amk = 0.0f;
+    uint32_t an = 0, ank = 0;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float x = elem<DT>(d[j], e);
+            if (x > -INFINITY && weight_bin(x, cc) > gstar) {
+                const float w = __builtin_amdgcn_exp2f(fmaf(x, cc, -rc));
+                const bool k = f32_key(x) >= kmin;
+                am += w;
+                ++an;
+                amk += k ? w : 0.0f;
+                ank += k ? 1u : 0u;
+            }
+        }
+        slot_fence();
+    }
+    opaque(d);
+    const double am_b = block_sum_f64(static_cast<double>(am), sm, 0);
+    const double amk_b = block_sum_f64(static_cast<double>(amk), sm, 1);
+    const uint32_t an_b = block_sum_u32(an, sm, 2);
+    const uint32_t ank_b = block_sum_u32(ank, sm, 3);
+    uint32_t nb = 0;
+    if (bin) {
+        nb = ordered_publish<DT, NL>(
+            d, sm, tbase, a.cand + (static_cast<int64_t>(b) * a.rec_stride + c) * kSplitCandStride + kSplitCap,
+            static_cast<uint32_t>(kSplitBinCap),
+            [&](float x) { return x > -INFINITY && weight_bin(x, cc) == gstar; }, [](float) {});
+    }
+    if (t == 0) {
+        st_dev_f64(&rec->am_all, am_b);
+        st_dev_f64(&rec->am_kept, amk_b);
+        st_dev(&rec->an_all, an_b);
+        st_dev(&rec->an_kept, ank_b);
+        st_dev(&rec->bcnt, nb);
     }
 }
 
@@ -1086,9 +1068,11 @@ __device__ __forceinline__ int32_t draw_in_chunk(const SampleArgs& a, FinSmem& f
     return tok;
 }
 
+// Finishes row b once every chunk has published (for histogram rows: both
+// publications; gstar and kmin are the finisher's decision).
 template <int DT, int NL>
 __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, int b, const RowParams& prm,
-                                           uint32_t mode, float cc, uint64_t word) {
+                                           uint32_t mode, float cc, uint64_t word, float gstar, uint32_t kmin) {
     using G = Geo<DT, NL>;
     FinSmem& f = sm.f;
     const int t = static_cast<int>(threadIdx.x);
@@ -1097,16 +1081,14 @@ __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, i
     const SplitRec* recs = a.rec + static_cast<int64_t>(b) * a.rec_stride;
 
     // the records
+    const __amdgpu_buffer_rsrc_t rr = l2_rsrc(recs, static_cast<uint32_t>(S) * sizeof(SplitRec));
     if (t < S) {
-        f.cm[t] = ld_dev_f32(&recs[t].m);
-        f.camax[t] = ld_dev(&recs[t].amax);
-        f.ctheta[t] = ld_dev_f32(&recs[t].theta);
-        f.ccnt[t] = ld_dev(&recs[t].cnt);
-        f.cz[t] = ld_dev_f64(&recs[t].z);
-        f.crc[t] = ld_dev_f32(&recs[t].rc);
-        f.cglo[t] = ld_dev_f32(&recs[t].glo);
-        f.cghi[t] = ld_dev_f32(&recs[t].ghi);
-        f.cwcnt[t] = ld_dev(&recs[t].wcnt);
+        f.cm[t] = l2_f32(rr, DST_REC_OFF(t, m));
+        f.camax[t] = l2_u32(rr, DST_REC_OFF(t, amax));
+        f.ctheta[t] = l2_f32(rr, DST_REC_OFF(t, theta));
+        f.ccnt[t] = l2_u32(rr, DST_REC_OFF(t, cnt));
+        f.cz[t] = l2_f64(rr, DST_REC_OFF(t, z));
+        f.crc[t] = l2_f32(rr, DST_REC_OFF(t, rc));
     }
     __syncthreads();
 
@@ -1203,7 +1185,9 @@ __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, i
     // takes 8 consecutive entries); returns how many passed.  side(chunk,
     // key) sees every entry once.
     auto load_list = [&](uint32_t raw_n, int region, auto keep, auto side) {
-        const uint64_t* cb = a.cand + static_cast<int64_t>(b) * a.rec_stride * kSplitCandStride + region;
+        const __amdgpu_buffer_rsrc_t cr =
+            l2_rsrc(a.cand + static_cast<int64_t>(b) * a.rec_stride * kSplitCandStride,
+                    static_cast<uint32_t>(S) * kSplitCandStride * sizeof(uint64_t));
         uint32_t L32 = 0;
         for (uint32_t batch = 0; batch < raw_n; batch += 8 * kT) {
             uint64_t v[8];
@@ -1212,17 +1196,14 @@ __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, i
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const uint32_t fi = batch + 8 * static_cast<uint32_t>(t) + q;
-                v[q] = 0ull;
-                ch[q] = 0;
-                if (fi < raw_n) {
-                    int lo = 0, hi = S - 1;       // the chunk c with coff[c] <= fi < coff[c + 1]
-                    while (lo < hi) {
-                        const int mid = (lo + hi + 1) >> 1;
-                        if (f.coff[mid] <= fi) lo = mid; else hi = mid - 1;
-                    }
-                    ch[q] = lo;
-                    v[q] = ld_dev(cb + static_cast<int64_t>(lo) * kSplitCandStride + (fi - f.coff[lo]));
+                int lo = 0, hi = S - 1;       // the chunk c with coff[c] <= fi < coff[c + 1]
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (f.coff[mid] <= fi) lo = mid; else hi = mid - 1;
                 }
+                ch[q] = lo;
+                const uint32_t e = static_cast<uint32_t>(lo) * kSplitCandStride + region + (fi - f.coff[lo]);
+                v[q] = l2_u64(cr, fi < raw_n ? e * 8u : kL2None);
             }
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
@@ -1275,11 +1256,114 @@ __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, i
     }
     if (mode == kModeFull) return;
 
+    if (mode == kModeHist) {
+        // ---- top-p and / or min_p through the weight histogram: the bin G*
+        // elements' cut, then the draw over the kept masses per chunk
+        const bool bin = prm.top_p;
+        const double target = static_cast<double>(prm.p) * zrow;
+        if (t < kWave) {
+            const bool has = t < S;
+            const int tc = has ? t : 1 << 20;   // past the buffer: reads 0
+            const double sc = has ? f.csc[t] : 0.0;
+            const double aa = l2_f64(rr, DST_REC_OFF(tc, am_all)) * sc;
+            const double ak = l2_f64(rr, DST_REC_OFF(tc, am_kept)) * sc;
+            const uint32_t na = l2_u32(rr, DST_REC_OFF(tc, an_all));
+            const uint32_t nk = l2_u32(rr, DST_REC_OFF(tc, an_kept));
+            const uint32_t bc = l2_u32(rr, DST_REC_OFF(tc, bcnt));
+            const bool over = has && bc > static_cast<uint32_t>(kSplitBinCap);
+            const uint32_t bcv = over ? 0u : bc;
+            const uint32_t incl = wave_scan_u32_dpp(bcv);
+            if (has) {
+                f.coff[t] = incl - bcv;
+                f.ckept[t] = ak;
+            }
+            const double A = wave_sum_dpp(aa);
+            const uint32_t NA = wave_sum_u32_dpp(na), NK = wave_sum_u32_dpp(nk);
+            const bool any_over = __ballot(over) != 0ull;
+            if (t == 0) {
+                f.list_n = readlane_u32(incl, S - 1);
+                f.amass = A;
+                f.anum = NA;
+                f.sel_c = NK;
+                f.bad = any_over ? 1u : 0u;
+            }
+        }
+        __syncthreads();
+        const double A = f.amass;
+        const uint32_t NA = f.anum, NK = f.sel_c;
+        bool hok = f.bad == 0u;
+        uint32_t Lb = 0;
+        if (hok && bin) {
+            Lb = load_list(f.list_n, kSplitCap, [](uint32_t) { return true; }, [](int, uint32_t) {});
+            hok = Lb <= static_cast<uint32_t>(kListMax);
+        }
+        if (hok) {
+            DCut cp{0u, 0xffffffffu};   // the top-p cut; without top-p the whole bin (it is empty)
+            if (bin) {
+                const Found fb = descent<true>(f, static_cast<int>(Lb), 0u, maxkey, DCut{0u, 0xffffffffu}, 0u,
+                                               target, NA, A);
+                if (fb.ok) cp = fb.cut;
+                else if (A >= target) cp = DCut{0xffffffffu, 0u};   // rounding moved the crossing above the bin
+                // else: rounding moved it below the bin, which is kept whole
+            }
+            const DCut fc = kmin > cp.key ? DCut{kmin, 0xffffffffu} : cp;
+            // the bin's kept elements: their count, and their mass per chunk
+            uint32_t bn = 0;
+            for (int i = t; i < static_cast<int>(Lb); i += kT) {
+                const uint32_t k = f.key[i];
+                if (k >= kmin && kept_by(fc, k, f.idx[i])) {
+                    ++bn;
+                    atomicAdd(&f.ckept[f.idx[i] / G::ELEMS], static_cast<double>(f.w[i]));
+                }
+            }
+            uint32_t ec, bn_all;
+            double em, tm2;
+            block_scan2(bn, 0.0, &ec, &em, &bn_all, &tm2, f);
+            if (t < kWave) {
+                const double kc = t < S ? f.ckept[t] : 0.0;
+                const double incl = wave_scan_f64_dpp(kc);
+                const double W = readlane_f64(incl, S - 1);
+                const uint64_t bal = __ballot(t < S && incl > u * W);
+                const int cs = bal ? __ffsll(static_cast<long long>(bal)) - 1 : S - 1;
+                const double before = readlane_f64(incl - kc, cs);
+                if (t == 0) {
+                    f.cstar = cs;
+                    f.before = before;
+                    f.zrow = W;   // the kept mass, relative to rref
+                }
+            }
+            __syncthreads();
+            const int cs = f.cstar;
+            const double W = f.zrow;
+            auto keptf = [&](uint32_t i, float x, uint32_t k) {
+                const float g = weight_bin(x, cc);
+                return k >= kmin && (g > gstar || (g == gstar && kept_by(fc, k, i)));
+            };
+            const int32_t tok =
+                draw_in_chunk<DT, NL>(a, f, b, cs, cc, f.crc[cs], f.csc[cs], f.before, u * W, keptf);
+            if (t == 0) {
+                a.tokens_out[b] = tok;
+                if (a.kept_out) a.kept_out[b] = static_cast<int32_t>(NK + bn_all);
+                if (a.rand_out) a.rand_out[b] = word;
+            }
+            if (a.probs_out) {
+                const double inv = 1.0 / W;
+                debug_probs<DT, NL>(a, b, keptf, [&](int c, float x) {
+                    return static_cast<float>(
+                        static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, cc, -f.crc[c]))) * f.csc[c] * inv);
+                });
+            }
+            return;
+        }
+        __syncthreads();
+        exact_row<DT, kT>(a, b, row_ptr(a, b, G::ES), prm, word, u, sm.e);
+        return;
+    }
+
     // ---- top-k, then top-p inside it, then min_p
     bool ok = !bad;
     DCut cut{0u, 0xffffffffu};
     bool kp_in_list = false;
-    bool flat = false;
     const bool has_k = prm.k < a.V;
     if (ok && has_k) {
         const Found fk = descent<false>(f, L, kappa, maxkey, cut, static_cast<uint32_t>(prm.k), 0.0);
@@ -1301,201 +1385,19 @@ __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, i
             wk = tm2;
         }
         const Found fp = descent<true>(f, L, kappa, maxkey, cut, 0u, static_cast<double>(prm.p) * wk);
-        if (fp.ok) {
-            cut = fp.cut;
-            kp_in_list = true;
-        } else if (!has_k) {
-            kp_in_list = false;   // the nucleus reaches below kappa
-            flat = !(prm.min_p > 0.0f);
-        }
+        kp_in_list = fp.ok;
+        if (fp.ok) cut = fp.cut;
     }
     if (ok && prm.min_p > 0.0f) {
         const double xm = static_cast<double>(m) + static_cast<double>(prm.T) * log(static_cast<double>(prm.min_p));
         const float xf = static_cast<float>(xm);
-        const uint32_t kmin = f32_key(xf) + (static_cast<double>(xf) < xm ? 1u : 0u);
+        const uint32_t km = f32_key(xf) + (static_cast<double>(xf) < xm ? 1u : 0u);
         if (kp_in_list) {
-            if (kmin > cut.key) cut = DCut{kmin, 0xffffffffu};
-        } else if (kmin >= kappa) {
-            cut = DCut{kmin, 0xffffffffu};
+            if (km > cut.key) cut = DCut{km, 0xffffffffu};
+        } else if (km >= kappa) {
+            cut = DCut{km, 0xffffffffu};
             kp_in_list = true;
         }
-    }
-
-    if (ok && !kp_in_list && flat) {
-        // ---- flat top-p row: the boundary weight bin from the chunks' windows
-        const double target = static_cast<double>(prm.p) * zrow;
-        // the windows' common bins [GLO, GHI], the mass above every window and
-        // where each chunk's window elements start
-        if (t < kWave) {
-            const bool has = t < S;
-            const float glo = has ? f.cglo[t] : 0.0f, ghi = has ? f.cghi[t] : 0.0f;
-            const bool nowin = has && !(glo <= ghi);
-            const float GLO = -wave_min_dpp(has ? -glo : INFINITY);
-            const float GHI = wave_min_dpp(has ? ghi : INFINITY);
-            const bool usable = __ballot(nowin) == 0ull && GLO <= GHI;
-            const double am = has && usable ? ld_dev_f64(&recs[t].above_m) * f.csc[t] : 0.0;
-            const uint32_t an = has && usable ? ld_dev(&recs[t].above_n) : 0u;
-            const double AM = wave_sum_dpp(am);
-            const uint32_t AN = wave_sum_u32_dpp(an);
-            const uint32_t wc = has && usable ? f.cwcnt[t] : 0u;
-            const uint32_t wi = wave_scan_u32_dpp(wc);
-            if (has) {
-                f.coff[t] = wi - wc;
-                f.ckept[t] = am;
-            }
-            if (t == 0) {
-                f.next = usable ? 1 : 0;
-                f.list_n = readlane_u32(wi, S - 1);
-                f.amass = AM;
-                f.anum = AN;
-                f.gwlo = GLO;
-                f.gwhi = GHI;
-            }
-        }
-        for (int i = t; i < kDBins; i += kT) {
-            f.hmass[i] = 0.0;
-            f.hcnt[i] = 0u;
-        }
-        __syncthreads();
-        if (f.next) {
-            const float GLO = f.gwlo, GHI = f.gwhi;
-            const uint32_t raw_n = f.list_n;
-            // the window elements' mass by bin over [GLO, GHI] (bin GHI - q at
-            // q) and above GHI (also per chunk: it is kept whatever the cut)
-            const uint64_t* cb = a.cand + static_cast<int64_t>(b) * a.rec_stride * kSplitCandStride + kSplitCap;
-            double up = 0.0;
-            uint32_t upn = 0;
-            for (uint32_t batch = 0; batch < raw_n; batch += 8 * kT) {
-                uint64_t v[8];
-                int ch[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const uint32_t fi = batch + 8 * static_cast<uint32_t>(t) + q;
-                    v[q] = 0ull;
-                    ch[q] = 0;
-                    if (fi < raw_n) {
-                        int lo = 0, hi = S - 1;
-                        while (lo < hi) {
-                            const int mid = (lo + hi + 1) >> 1;
-                            if (f.coff[mid] <= fi) lo = mid; else hi = mid - 1;
-                        }
-                        ch[q] = lo;
-                        v[q] = ld_dev(cb + static_cast<int64_t>(lo) * kSplitCandStride + (fi - f.coff[lo]));
-                    }
-                }
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const uint32_t fi = batch + 8 * static_cast<uint32_t>(t) + q;
-                    const float x = key_f32(static_cast<uint32_t>(v[q] >> 32));
-                    const float g = weight_bin(x, cc);
-                    const double w = static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, cc, -rref)));
-                    if (fi < raw_n && g > GHI) {
-                        up += w;
-                        ++upn;
-                        atomicAdd(&f.ckept[ch[q]], w);
-                    } else if (fi < raw_n && g >= GLO) {
-                        const int qb = static_cast<int>(GHI - g);
-                        atomicAdd(&f.hmass[qb], w);
-                        atomicAdd(&f.hcnt[qb], 1u);
-                    }
-                }
-            }
-            uint32_t e0, upn_all;
-            double e1, up_all;
-            block_scan2(upn, up, &e0, &e1, &upn_all, &up_all, f);   // ends with a barrier
-            // D(g), the mass of the bins >= g, first reaches the target at the
-            // row's boundary bin G*, which must lie in [GLO, GHI]: D(GHI + 1) <
-            // target <= D(G*).  Thread t owns bins q = 2t, 2t + 1.
-            const double above = f.amass + up_all;
-            const uint32_t above_n = f.anum + upn_all;
-            const double h0 = f.hmass[2 * t], h1 = f.hmass[2 * t + 1];
-            const uint32_t c0 = f.hcnt[2 * t], c1 = f.hcnt[2 * t + 1];
-            uint32_t ec, tc;
-            double em, tm;
-            block_scan2(c0 + c1, h0 + h1, &ec, &em, &tc, &tm, f);
-            if (t == 0) f.next = 0;
-            __syncthreads();
-            const double base = above + em;
-            const int nb = static_cast<int>(GHI - GLO) + 1;
-            if (base < target && base + h0 >= target && 2 * t < nb) {
-                f.next = 1;
-                f.gstar = GHI - static_cast<float>(2 * t);
-                f.amass = base;
-                f.anum = above_n + ec;
-            } else if (base + h0 < target && base + h0 + h1 >= target && 2 * t + 1 < nb) {
-                f.next = 1;
-                f.gstar = GHI - static_cast<float>(2 * t + 1);
-                f.amass = base + h0;
-                f.anum = above_n + ec + c0;
-            }
-            __syncthreads();
-        }
-        if (f.next) {
-            const float gstar = f.gstar, GHI = f.gwhi;
-            const double A = f.amass;
-            const uint32_t N = f.anum;
-            // the boundary bin's elements, from the windows; the windows' mass in
-            // (G*, GHI] joins the kept mass of its chunk
-            const uint32_t Lw = load_list(
-                f.list_n, kSplitCap, [&](uint32_t k) { return weight_bin(key_f32(k), cc) == gstar; },
-                [&](int c, uint32_t k) {
-                    const float x = key_f32(k);
-                    const float g = weight_bin(x, cc);
-                    if (g > gstar && g <= GHI)
-                        atomicAdd(&f.ckept[c], static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, cc, -rref))));
-                });
-            if (Lw <= static_cast<uint32_t>(kListMax)) {
-                const int Lb = static_cast<int>(Lw);
-                const Found fb = descent<true>(f, Lb, 1u, maxkey, DCut{0u, 0xffffffffu}, 0u, target, N, A);
-                if (fb.ok) {
-                    const DCut bc = fb.cut;
-                    // kept bin-G* mass per chunk
-                    for (int i = t; i < Lb; i += kT) {
-                        if (kept_by(bc, f.key[i], f.idx[i]))
-                            atomicAdd(&f.ckept[f.idx[i] / G::ELEMS], static_cast<double>(f.w[i]));
-                    }
-                    __syncthreads();
-                    if (t < kWave) {
-                        const double kc = t < S ? f.ckept[t] : 0.0;
-                        const double incl = wave_scan_f64_dpp(kc);
-                        const double W = readlane_f64(incl, S - 1);
-                        const double tgt = u * W;
-                        const uint64_t bal = __ballot(t < S && incl > tgt);
-                        const int cs = bal ? __ffsll(static_cast<long long>(bal)) - 1 : S - 1;
-                        const double before = readlane_f64(incl - kc, cs);
-                        if (t == 0) {
-                            f.cstar = cs;
-                            f.before = before;
-                            f.zrow = W;   // kept mass (relative to rref)
-                        }
-                    }
-                    __syncthreads();
-                    const int cs = f.cstar;
-                    const double W = f.zrow;
-                    auto keptf = [&](uint32_t i, float x, uint32_t k) {
-                        const float g = weight_bin(x, cc);
-                        return g > gstar || (g == gstar && kept_by(bc, k, i));
-                    };
-                    const int32_t tok = draw_in_chunk<DT, NL>(a, f, b, cs, cc, f.crc[cs], f.csc[cs], f.before,
-                                                              u * W, keptf);
-                    if (t == 0) {
-                        a.tokens_out[b] = tok;
-                        if (a.kept_out) a.kept_out[b] = static_cast<int32_t>(fb.n);
-                        if (a.rand_out) a.rand_out[b] = word;
-                    }
-                    if (a.probs_out) {
-                        const double inv = 1.0 / W;
-                        debug_probs<DT, NL>(a, b, keptf, [&](int c, float x) {
-                            return static_cast<float>(
-                                static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, cc, -f.crc[c]))) * f.csc[c] *
-                                inv);
-                        });
-                    }
-                    return;
-                }
-            }
-        }
-        ok = false;
     }
 
     ok = ok && kp_in_list;
@@ -1562,6 +1464,167 @@ __device__ __forceinline__ void finish_row(const SampleArgs& a, SplitSmem& sm, i
     }
 }
 
+// The min_p threshold as an order key: the smallest key whose value is
+// >= m + T ln(min_p) (computed in fp64).
+__device__ __forceinline__ uint32_t min_p_key(float m, const RowParams& prm) {
+    const double xm = static_cast<double>(m) + static_cast<double>(prm.T) * log(static_cast<double>(prm.min_p));
+    const float xf = static_cast<float>(xm);
+    return f32_key(xf) + (static_cast<double>(xf) < xm ? 1u : 0u);
+}
+
+struct HistDec {
+    float gstar;     // the row's boundary weight bin (-inf: no top-p)
+    uint32_t kmin;   // min_p key (0: none)
+    bool go;         // false: the histogram could not place the boundary
+};
+
+// The finisher's decision for a histogram row, from the chunks' first
+// publication: the row's histogram (the chunks' bins shifted onto the row's
+// grid, scaled to the row maximum; every chunk's deepest bin, which holds
+// all its deeper weights, left out), the bin G* where the descending mass
+// first reaches p of the row's, and the min_p key.  Published to the row's
+// decision word (data, then the epoch once the data stores have completed).
+template <int DT, int NL>
+__device__ __forceinline__ HistDec hist_decide(const SampleArgs& a, FinSmem& f, int b, const RowParams& prm,
+                                               float cc) {
+    const int t = static_cast<int>(threadIdx.x);
+    const int S = a.chunks;
+    const SplitRec* recs = a.rec + static_cast<int64_t>(b) * a.rec_stride;
+    if (t < kWave) {
+        const bool has = t < S;
+        const __amdgpu_buffer_rsrc_t rr = l2_rsrc(recs, static_cast<uint32_t>(S) * sizeof(SplitRec));
+        const int tc = has ? t : 1 << 20;
+        const float cm0 = l2_f32(rr, DST_REC_OFF(tc, m));
+        const float crc = l2_f32(rr, DST_REC_OFF(tc, rc));
+        const double cz = l2_f64(rr, DST_REC_OFF(tc, z));
+        const float cm = has ? cm0 : -INFINITY;
+        const float m = wave_max_dpp(cm);
+        const float rref = m * cc;
+        const double sc = has && cm > -INFINITY ? exp2(static_cast<double>(crc) - static_cast<double>(rref)) : 0.0;
+        const double zrow = wave_sum_dpp(cz * sc);
+        if (has) {
+            f.csc[t] = sc;
+            f.cm[t] = cm;
+        }
+        if (t == 0) {
+            f.zrow = zrow;
+            f.maxkey = f32_key(m);
+            f.sel_bin = -1;
+        }
+    }
+    __syncthreads();
+    const float m = key_f32(f.maxkey);
+    HistDec d{-INFINITY, 0u, true};
+    if (prm.top_p) {
+        const float gtop = weight_bin(m, cc);
+        // thread t sums the row's bins q = 4t .. 4t + 3 (bin gtop - q), four
+        // chunks' loads in flight at a time
+        double acc[4] = {0.0, 0.0, 0.0, 0.0};
+        const __amdgpu_buffer_rsrc_t hr = l2_rsrc(a.hist + static_cast<int64_t>(b) * a.rec_stride * kWBins,
+                                                  static_cast<uint32_t>(S) * kWBins * sizeof(float));
+        for (int c0 = 0; c0 < S; c0 += 8) {
+            float v[8][4];
+#pragma unroll
+            for (int cq = 0; cq < 8; ++cq) {
+                const int c = c0 + cq;
+                const float shf = c < S ? gtop - weight_bin(f.cm[c], cc) : INFINITY;
+                const int sh = shf < static_cast<float>(kWBins) ? static_cast<int>(shf) : kWBins;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * t + j - sh;
+                    const bool in = r >= 0 && r < kWBins - 1;
+                    v[cq][j] = l2_f32(hr, in ? static_cast<uint32_t>(c * kWBins + r) * 4u : kL2None);
+                }
+            }
+#pragma unroll
+            for (int cq = 0; cq < 8; ++cq) {
+                const double sc = c0 + cq < S ? f.csc[c0 + cq] : 0.0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] += static_cast<double>(v[cq][j]) * sc;
+            }
+        }
+        if (t == kT - 1) acc[3] = 0.0;   // the row's deepest bin
+        const double own = acc[0] + acc[1] + acc[2] + acc[3];
+        uint32_t ec, tc;
+        double em, tm;
+        block_scan2(0u, own, &ec, &em, &tc, &tm, f);
+        const double target = static_cast<double>(prm.p) * f.zrow;
+        double cum = em;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (cum < target && cum + acc[j] >= target) f.sel_bin = 4 * t + j;
+            cum += acc[j];
+        }
+        __syncthreads();
+        const int qs = f.sel_bin;
+        d.go = qs >= 0;
+        d.gstar = gtop - static_cast<float>(qs);
+    }
+    if (prm.min_p > 0.0f) d.kmin = min_p_key(m, prm);
+    if (t == 0) {
+        uint32_t* dw = a.dec + static_cast<int64_t>(b) * 4;
+        st_dev(dw + 1, __float_as_uint(d.gstar));
+        st_dev(dw + 2, d.kmin);
+        st_dev(dw + 3, d.go ? 1u : 2u);
+        wait_all_memory();
+        st_dev(dw, a.epoch);
+    }
+    __syncthreads();
+    return d;
+}
+
+// A histogram row's decision word, as a chunk reads it (thread 0 polls,
+// bounded); go is false on an abort or when the wait runs out.
+__device__ __forceinline__ HistDec wait_decision(const SampleArgs& a, int b, ChunkSmem& sm) {
+    if (threadIdx.x == 0) {
+        const uint32_t* dw = a.dec + static_cast<int64_t>(b) * 4;
+        uint32_t st = 0, g = 0, km = 0;
+        for (int spin = 0; spin < kSpinLimit; ++spin) {
+            if (ld_dev(dw) == a.epoch) {
+                asm volatile("" ::: "memory");   // the data loads stay after the epoch load
+                const __amdgpu_buffer_rsrc_t r = l2_rsrc(dw, 16);
+                g = l2_u32(r, 4);
+                km = l2_u32(r, 8);
+                st = l2_u32(r, 12);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        sm.wtot[0][0] = st;
+        sm.wtot[0][1] = g;
+        sm.wtot[0][2] = km;
+    }
+    __syncthreads();
+    const HistDec d{__uint_as_float(sm.wtot[0][1]), sm.wtot[0][2], sm.wtot[0][0] == 1u};
+    __syncthreads();
+    return d;
+}
+
+// Waits (bounded) until the row's other chunks have flagged `value`; true
+// when one of them never did.
+__device__ __forceinline__ bool wait_flags(const SampleArgs& a, int b, uint32_t value, SplitSmem& sm) {
+    const int S = a.chunks;
+    if (threadIdx.x < kWave) {
+        const int lane = lane_id();
+        const uint32_t* fl = a.flags + static_cast<int64_t>(b) * kSplitMaxChunks;
+        int late = 0;
+        for (int spin = 0;; ++spin) {
+            const uint32_t fv = lane < S - 1 ? ld_dev(fl + lane) : value;
+            if (__ballot(fv != value) == 0ull) break;
+            if (spin >= kSpinLimit) {
+                late = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (lane == 0) sm.f.next = late;
+    }
+    __syncthreads();
+    const bool late = sm.f.next != 0;
+    __syncthreads();
+    return late;
+}
+
 template <int DT, int NL>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(DST_SPLIT_WAVES_PER_EU, 8)))
 void sample_split_kernel(SampleArgs a) {
@@ -1588,7 +1651,6 @@ void sample_split_kernel(SampleArgs a) {
     // rank every chunk must cover whatever its length
     uint32_t mode;
     int jrank = 0, jmin = 0;
-    float flat_p = 0.0f;
     if (prm.greedy || prm.k == 1) {
         mode = kModeArgmax;
     } else if (prm.k < a.V && prm.k <= kKList) {
@@ -1599,10 +1661,8 @@ void sample_split_kernel(SampleArgs a) {
         jrank = jtopp;
         jmin = prm.k;
     } else if (prm.top_p || prm.min_p > 0.0f) {
-        mode = kModeTopP;
-        jrank = jtopp;
-        jmin = dbg_list ? kJDebug : 1;
-        flat_p = prm.top_p && !(prm.min_p > 0.0f) ? prm.p : 0.0f;
+        mode = kModeHist;
+        jrank = jmin = dbg_list ? kJDebug : 0;
     } else {
         mode = kModeFull;
         jrank = jmin = dbg_list ? kJDebug : 0;
@@ -1617,39 +1677,52 @@ void sample_split_kernel(SampleArgs a) {
         return;
     }
 
-    chunk_phase<DT, NL>(a, sm.c, b, c_own, mode, cc, jrank, jmin, flat_p);
+    u32x4_t_ d[NL];
+    load_chunk<DT, NL>(a, b, c_own, d);
+    const float rc = chunk_phase<DT, NL>(a, sm.c, b, c_own, d, mode, cc, jrank, jmin,
+                                         mode == kModeHist && prm.top_p);
     wait_all_memory();
     __syncthreads();
+    uint32_t* own_flag = a.flags + static_cast<int64_t>(b) * kSplitMaxChunks + c_own;
     if (!finisher) {
-        if (threadIdx.x == 0) st_dev(a.flags + static_cast<int64_t>(b) * kSplitMaxChunks + c_own, a.epoch);
+        if (threadIdx.x == 0) st_dev(own_flag, a.epoch);
+        if (mode != kModeHist) return;
+        // a histogram row's chunk: the second publication, once decided
+        const HistDec hd = wait_decision(a, b, sm.c);
+        if (!hd.go) return;
+        hist_phase2<DT, NL>(a, sm.c, b, c_own, d, cc, rc, hd.gstar, hd.kmin, prm.top_p);
+        wait_all_memory();
+        __syncthreads();
+        if (threadIdx.x == 0) st_dev(own_flag, a.epoch + 1u);
         return;
     }
-    // the finisher waits for the row's other chunks (bounded)
-    if (threadIdx.x < kWave) {
-        const int lane = lane_id();
-        const uint32_t* fl = a.flags + static_cast<int64_t>(b) * kSplitMaxChunks;
-        int late = 0;
-        for (int spin = 0;; ++spin) {
-            const uint32_t fv = lane < S - 1 ? ld_dev(fl + lane) : a.epoch;
-            if (__ballot(fv != a.epoch) == 0ull) break;
-            if (spin >= kSpinLimit) {
-                late = 1;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        if (lane == 0) sm.f.next = late;
-    }
-    __syncthreads();
-    const bool late = sm.f.next != 0;
-    __syncthreads();
+    // the finisher: waits for the row's other chunks (bounded); a chunk that
+    // never published sends the row to the exact routine, which reads it
     const uint64_t word = a.temperature ? request_word(a.seed, ld_global<int64_t>(a.uid + b), a.step) : 0ull;
+    bool late = wait_flags(a, b, a.epoch, sm);
+    HistDec hd{-INFINITY, 0u, true};
+    if (mode == kModeHist) {
+        if (!late) {
+            hd = hist_decide<DT, NL>(a, sm.f, b, prm, cc);
+        } else if (threadIdx.x == 0) {
+            uint32_t* dw = a.dec + static_cast<int64_t>(b) * 4;
+            st_dev(dw + 3, 2u);   // abort: the other chunks stop waiting
+            wait_all_memory();
+            st_dev(dw, a.epoch);
+        }
+        if (!late && hd.go) {
+            hist_phase2<DT, NL>(a, sm.c, b, c_own, d, cc, rc, hd.gstar, hd.kmin, prm.top_p);
+            wait_all_memory();
+            __syncthreads();
+            late = wait_flags(a, b, a.epoch + 1u, sm);
+        }
+        late = late || !hd.go;
+    }
     if (late) {
-        // a chunk never published within the wait: the exact routine reads the row itself
         exact_row<DT, kT>(a, b, row_ptr(a, b, Geo<DT, NL>::ES), prm, word, uniform24(word), sm.e);
         return;
     }
-    finish_row<DT, NL>(a, sm, b, prm, mode, cc, word);
+    finish_row<DT, NL>(a, sm, b, prm, mode, cc, word, hd.gstar, hd.kmin);
 }
 
 template <int DT, int NL>

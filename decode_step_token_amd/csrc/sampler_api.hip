@@ -31,6 +31,9 @@ constexpr unsigned kEventFlags = hipEventDisableTiming | hipEventDisableSystemFe
 constexpr size_t kPageRecordBytes = 4 * sizeof(int64_t);
 // one thread per gathered entry: a dispatch holds fewer than 2^32 work-items
 constexpr int64_t kMaxGather = INT32_MAX;
+// all-greedy batches with at least this many rows fill the GPU with one
+// workgroup per row and take the single-pass kernel; smaller ones split rows
+constexpr int kStreamGreedyMinRows = 256;
 
 struct DeviceGuard {
     int prev = -1;
@@ -54,9 +57,14 @@ struct dst_sampler {
     int dtype = 0;
     uint64_t seed = 0;
     int cus = 0;                       // compute units: stream blocks resident at once
-    void* workspace = nullptr;       // device: split-row records, candidates and flags
+    void* argmax_ws = nullptr;         // device: argmax slots and counters
+    uint64_t* slot = nullptr;
+    uint32_t* count = nullptr;
+    void* workspace = nullptr;       // device: split-row records, candidates, histograms, flags
     dst::SplitRec* rec = nullptr;
     uint64_t* cand = nullptr;
+    float* hist = nullptr;
+    uint32_t* dec = nullptr;
     uint32_t* flags = nullptr;
     int split_nl = 0;                  // loads per thread and chunk (0: rows go to the exact kernel)
     int split_chunks = 0;              // chunks per row
@@ -123,6 +131,7 @@ int sampler_destroy(dst_sampler* s) {
     for (auto& e : s->pt_ev)
         if (e) (void)hipEventDestroy(e);
     if (s->workspace) (void)hipFree(s->workspace);
+    if (s->argmax_ws) (void)hipFree(s->argmax_ws);
     if (s->status_host) (void)hipHostFree(s->status_host);
     if (s->prep_host) (void)hipHostFree(s->prep_host);
     if (s->pt_host) (void)hipHostFree(s->pt_host);
@@ -155,17 +164,30 @@ int sampler_create(dst_sampler** out, int device, int32_t max_batch, int32_t voc
         s->cus = 0;                    // unknown: rows keep their index order
     }
 
-    // split-row workspace: per (row, chunk) a record and a candidate block,
-    // per row one cache line of epoch flags (zero: nothing published yet)
+    // split-row workspace: per (row, chunk) a record, a candidate block and a
+    // weight histogram; per row a decision word and one cache line of epoch
+    // flags (zero: nothing published yet)
     s->split_nl = dst::split_plan(vocab_size, logits_dtype, &s->split_chunks);
     const size_t rows = static_cast<size_t>(max_batch);
     const size_t nrec = rows * static_cast<size_t>(s->split_nl ? s->split_chunks : 0);
     const size_t rec_bytes = nrec * sizeof(dst::SplitRec);
     const size_t cand_bytes = nrec * dst::kSplitCandStride * sizeof(uint64_t);
+    const size_t hist_bytes = nrec * dst::kSplitHistBins * sizeof(float);
+    const size_t dec_bytes = rows * 4 * sizeof(uint32_t);
     const size_t flag_bytes = rows * dst::kSplitMaxChunks * sizeof(uint32_t);
-    hipError_t e = hipSuccess;
-    if (s->split_nl) {
-        e = hipMalloc(&s->workspace, rec_bytes + cand_bytes + flag_bytes);
+    const size_t slot_bytes = sizeof(uint64_t) * rows;
+    const size_t count_bytes = sizeof(uint32_t) * rows;
+    hipError_t e = hipMalloc(&s->argmax_ws, slot_bytes + count_bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        sampler_destroy(s);
+        return SAMPLER_ENOMEM;
+    }
+    s->slot = static_cast<uint64_t*>(s->argmax_ws);
+    s->count = reinterpret_cast<uint32_t*>(static_cast<char*>(s->argmax_ws) + slot_bytes);
+    e = hipMemset(s->argmax_ws, 0, slot_bytes + count_bytes);
+    if (e == hipSuccess && s->split_nl) {
+        e = hipMalloc(&s->workspace, rec_bytes + cand_bytes + hist_bytes + dec_bytes + flag_bytes);
         if (e != hipSuccess) {
             (void)hipGetLastError();
             sampler_destroy(s);
@@ -174,8 +196,10 @@ int sampler_create(dst_sampler** out, int device, int32_t max_batch, int32_t voc
         char* ws = static_cast<char*>(s->workspace);
         s->rec = reinterpret_cast<dst::SplitRec*>(ws);
         s->cand = reinterpret_cast<uint64_t*>(ws + rec_bytes);
-        s->flags = reinterpret_cast<uint32_t*>(ws + rec_bytes + cand_bytes);
-        e = hipMemset(s->flags, 0, flag_bytes);
+        s->hist = reinterpret_cast<float*>(ws + rec_bytes + cand_bytes);
+        s->dec = reinterpret_cast<uint32_t*>(ws + rec_bytes + cand_bytes + hist_bytes);
+        s->flags = reinterpret_cast<uint32_t*>(ws + rec_bytes + cand_bytes + hist_bytes + dec_bytes);
+        e = hipMemset(s->dec, 0, dec_bytes + flag_bytes);
     }
     if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&s->status_host), sizeof(uint32_t),
                                            hipHostMallocMapped);
@@ -224,7 +248,31 @@ int sample_batch(dst_sampler* s, void* stream, const void* logits, int64_t row_s
     DeviceGuard g(s->device);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    {
+    const uint32_t flags = dbg ? dbg->flags : 0u;
+    const uint32_t forced = flags & (SAMPLER_DEBUG_FORCE_EXACT | SAMPLER_DEBUG_FORCE_STREAM | SAMPLER_DEBUG_FORCE_SPLIT);
+    // the split-row kernel reads rows with 16-byte loads: the logits and every
+    // row start must be 16-byte aligned, and the vocabulary within its chunk count
+    const int64_t esize = s->dtype == SAMPLER_F32 ? 4 : 2;
+    const bool aligned = (reinterpret_cast<uintptr_t>(logits) & 15u) == 0 && ((row_stride * esize) & 15) == 0;
+    const bool split_ok = s->split_nl && aligned;
+    if (!forced && !temperature && B < kStreamGreedyMinRows) {
+        dst::ArgmaxArgs a{};
+        a.logits = logits;
+        a.row_stride = row_stride;
+        a.B = B;
+        a.V = s->vocab;
+        dst::argmax_plan(B, s->vocab, s->dtype, &a.chunks, &a.chunk_len);
+        a.slot = s->slot;
+        a.count = s->count;
+        a.tokens_out = tokens_out;
+        if (dbg) {
+            a.probs_out = dbg->probs_out;
+            a.kept_out = dbg->kept_out;
+            a.topk_idx_out = dbg->topk_idx_out;
+            a.rand_out = dbg->rand_out;
+        }
+        e = dst::launch_argmax(a, s->dtype, st);
+    } else {
         dst::SampleArgs a{};
         a.logits = logits;
         a.row_stride = row_stride;
@@ -245,22 +293,24 @@ int sample_batch(dst_sampler* s, void* stream, const void* logits, int64_t row_s
             a.topk_idx_out = dbg->topk_idx_out;
             a.rand_out = dbg->rand_out;
         }
-        // the split-row kernel reads rows with 16-byte loads: the logits and
-        // every row start must be 16-byte aligned; other layouts, and
-        // vocabularies beyond its chunk count, take the exact kernel
-        const int64_t esize = s->dtype == SAMPLER_F32 ? 4 : 2;
-        const bool aligned = (reinterpret_cast<uintptr_t>(logits) & 15u) == 0 && ((row_stride * esize) & 15) == 0;
-        if ((dbg && (dbg->flags & SAMPLER_DEBUG_FORCE_EXACT)) || !s->split_nl || !aligned) {
+        // batches of fewer rows than half the compute units spread each row
+        // over many workgroups; larger ones give each row a workgroup
+        const bool small = s->cus > 0 ? 2 * B < s->cus : B < 128;
+        if (flags & SAMPLER_DEBUG_FORCE_EXACT) {
             e = dst::launch_sample_exact(a, s->dtype, st);
-        } else {
+        } else if (split_ok && ((flags & SAMPLER_DEBUG_FORCE_SPLIT) || (!(flags & SAMPLER_DEBUG_FORCE_STREAM) && small))) {
             a.rec = s->rec;
             a.cand = s->cand;
+            a.hist = s->hist;
+            a.dec = s->dec;
             a.flags = s->flags;
             a.rec_stride = s->split_chunks;
             a.chunks = s->split_chunks;
-            s->epoch = s->epoch + 1u == 0u ? 1u : s->epoch + 1u;
+            s->epoch = s->epoch + 2u == 0u ? 2u : s->epoch + 2u;
             a.epoch = s->epoch;
             e = dst::launch_sample_split(a, s->dtype, s->split_nl, st);
+        } else {
+            e = dst::launch_sample_stream(a, s->dtype, st);
         }
     }
     if (e != hipSuccess) return fail(s, SAMPLER_EHIP, "sample_batch: launch", e);

@@ -76,6 +76,12 @@ enum sampler_status {
 /* sampler_debug.flags: run every row through the exact multi-pass path
  * (re-reads each row several times) instead of the single-pass kernel. */
 #define SAMPLER_DEBUG_FORCE_EXACT 1u
+/* ... through the one-workgroup-per-row kernel (batches of at least half as
+ * many rows as compute units take it by default). */
+#define SAMPLER_DEBUG_FORCE_STREAM 2u
+/* ... through the split-row kernel (smaller batches take it by default; a
+ * misaligned logits pointer or row stride falls back to the per-row kernel). */
+#define SAMPLER_DEBUG_FORCE_SPLIT 4u
 
 /*
  * Optional per-call debug outputs (tests only; each field may be NULL; every
@@ -89,7 +95,9 @@ enum sampler_status {
  *                for greedy rows the argmax then -1.
  *   rand_out     [B] uint64: the Philox word the row's uniform comes from
  *                (0 when the batch has no temperature array).
- *   flags        host value: 0, or SAMPLER_DEBUG_FORCE_EXACT.
+ *   flags        host value: 0, or one of SAMPLER_DEBUG_FORCE_EXACT,
+ *                SAMPLER_DEBUG_FORCE_STREAM, SAMPLER_DEBUG_FORCE_SPLIT (all-greedy
+ *                batches of fewer than 256 rows otherwise take the argmax kernel).
  */
 typedef struct sampler_debug {
     float*    probs_out;

@@ -44,8 +44,12 @@ def opt(a, dtype):
 
 
 def run_gpu(w: Workload, sampler: dst.Sampler = None, debug: bool = True, pad: int = 0,
-            host: bool = True, logits_dev: torch.Tensor = None, force_exact: bool = False):
-    """Run sample_batch + write_tokens for one step; returns numpy results."""
+            host: bool = True, logits_dev: torch.Tensor = None, force_exact: bool = False,
+            path: str = None):
+    """Run sample_batch + write_tokens for one step; returns numpy results.
+    ``path``: None (the library's choice), "exact", "stream" or "split"."""
+    if force_exact:
+        path = "exact"
     own = sampler is None
     if own:
         sampler = dst.Sampler(0, max(w.B, 1), w.V, w.dtype, w.seed)
@@ -62,8 +66,9 @@ def run_gpu(w: Workload, sampler: dst.Sampler = None, debug: bool = True, pad: i
                    "kept_out": torch.full((B,), -7, dtype=torch.int32, device="cuda"),
                    "topk_idx_out": torch.full((B, 64), -7, dtype=torch.int32, device="cuda"),
                    "rand_out": torch.full((B,), -7, dtype=torch.int64, device="cuda")}
-        if force_exact:
-            dbg = dict(dbg or {}, force_exact=True)
+        if path is not None:
+            assert path in ("exact", "stream", "split"), path
+            dbg = dict(dbg or {}, **{f"force_{path}": True})
         toks = sampler.sample(logits, temperature=T, top_k=k, top_p=p, uid=uid, step=w.step,
                               debug=dbg, min_p=opt(w.min_p, torch.float32))
         pool = torch.from_numpy(w.pool.copy()).cuda()

@@ -27,8 +27,8 @@ def _gpu():
 
 def _check(w, **kw):
     log(f"case {w.name} B={w.B} V={w.V} dtype={w.dtype} step={w.step} "
-        f"{'exact path' if kw.get('force_exact') else ''}")
-    gpu = run_gpu(w, **{k: v for k, v in kw.items() if k in ("pad", "debug", "force_exact")})
+        f"{'exact path' if kw.get('force_exact') else ''}{kw.get('path') or ''}")
+    gpu = run_gpu(w, **{k: v for k, v in kw.items() if k in ("pad", "debug", "force_exact", "path")})
     ref = run_oracle(w)
     stats = compare(w, gpu, ref, check_probs_rows=kw.get("probs_rows"))
     log(f"  ok {stats}")
