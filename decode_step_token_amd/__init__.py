@@ -10,13 +10,13 @@ ctypes binding.
 """
 from ._binding import (EXPORTS, LIB_PATH, SAMPLER_BF16, SAMPLER_DEBUG_TOPK, SAMPLER_F32, Sampler,
                        SamplerArgs, SamplerDebug, SamplerError, gather_tokens, load, sample_batch,
-                       sampler_check, sampler_create, sampler_destroy, sampler_prepare,
+                       sample_batch_static, sampler_check, sampler_create, sampler_destroy, sampler_prepare,
                        sampler_query, sampler_strerror, sampler_wait, write_page_table,
                        write_tokens)
 
 __all__ = [
     "EXPORTS", "LIB_PATH", "SAMPLER_BF16", "SAMPLER_DEBUG_TOPK", "SAMPLER_F32", "Sampler",
     "SamplerArgs", "SamplerDebug", "SamplerError", "gather_tokens", "load", "sample_batch",
-    "sampler_check", "sampler_create", "sampler_destroy", "sampler_prepare", "sampler_query",
+    "sample_batch_static", "sampler_check", "sampler_create", "sampler_destroy", "sampler_prepare", "sampler_query",
     "sampler_strerror", "sampler_wait", "write_page_table", "write_tokens",
 ]

@@ -29,7 +29,8 @@ SAMPLER_DEBUG_FORCE_SPLIT = 4
 STATUS = {0: "SAMPLER_OK", -1: "SAMPLER_EINVAL", -2: "SAMPLER_ENOMEM", -3: "SAMPLER_EHIP",
           -4: "SAMPLER_ENOTPINNED", -5: "SAMPLER_EDEVICE", -6: "SAMPLER_ETICKET"}
 
-EXPORTS = ("sampler_create", "sampler_destroy", "sampler_prepare", "sample_batch", "write_tokens",
+EXPORTS = ("sampler_create", "sampler_destroy", "sampler_prepare", "sample_batch",
+           "sample_batch_static", "write_tokens",
            "gather_tokens", "write_page_table", "sampler_wait", "sampler_query", "sampler_check",
            "sampler_strerror", "sampler_last_error")
 
@@ -72,6 +73,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sampler_destroy.argtypes = [P]
     lib.sample_batch.argtypes = [P, P, P, I64, I32, P, P, P, P, P, U64, P,
                                  ctypes.POINTER(SamplerDebug)]
+    lib.sample_batch_static.argtypes = [INT, P, P, I64, I32, I32, I32, U64, P, P, P, P, P, U64, P]
     lib.write_tokens.argtypes = [P, P, P, I64, I64, P, P, P, I32, P, ctypes.POINTER(U64)]
     lib.gather_tokens.argtypes = [P, P, P, I64, I64, P, P, I64, P]
     lib.write_page_table.argtypes = [P, P, P, I64, I64, P, P, P, I32, P, I64, I32]
@@ -84,7 +86,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sampler_last_error.argtypes = [P]
     lib.sampler_last_error.restype = ctypes.c_char_p
     for name in ("sampler_create", "sampler_destroy", "sampler_prepare", "sample_batch",
-                 "write_tokens", "gather_tokens", "write_page_table", "sampler_wait",
+                 "sample_batch_static", "write_tokens", "gather_tokens", "write_page_table", "sampler_wait",
                  "sampler_query", "sampler_check"):
         getattr(lib, name).restype = INT
     _lib = lib
@@ -176,6 +178,38 @@ def sample_batch(handle, logits: torch.Tensor, temperature=None, top_k=None, top
         _ptr(tokens_out, "tokens_out", torch.int32, None, dev),
         ctypes.byref(dbg) if dbg is not None else None)
     _check(code, "sample_batch", handle)
+    return tokens_out
+
+
+def sample_batch_static(logits: torch.Tensor, vocab_size: int, dtype: str, seed: int,
+                        temperature=None, top_k=None, top_p=None, uid=None, step: int = 0,
+                        tokens_out: Optional[torch.Tensor] = None, stream=None,
+                        min_p=None) -> torch.Tensor:
+    """The entry point that allocates nothing (no handle; at most 64 rows).
+    ``logits``: [B, >=vocab_size] on a GPU; returns (or fills) ``tokens_out``."""
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be 2-D [B, V] with contiguous rows")
+    want = (torch.float32,) if dtype == "f32" else (torch.bfloat16, torch.int16, torch.uint16)
+    if logits.dtype not in want:
+        raise TypeError(f"logits: expected {dtype}, got {logits.dtype}")
+    if logits.shape[1] < vocab_size:
+        raise ValueError(f"logits rows hold {logits.shape[1]} < vocab_size {vocab_size} entries")
+    dev = logits.device
+    B = logits.shape[0]
+    if tokens_out is None:
+        tokens_out = torch.empty(B, dtype=torch.int32, device=dev)
+    code = load().sample_batch_static(
+        int(dev.index or 0), _stream(stream), ctypes.c_void_p(logits.data_ptr()), logits.stride(0), B,
+        int(vocab_size), SAMPLER_F32 if dtype == "f32" else SAMPLER_BF16, int(seed) & ((1 << 64) - 1),
+        _ptr(temperature, "temperature", torch.float32, B, dev),
+        _ptr(top_k, "top_k", torch.int32, B, dev),
+        _ptr(top_p, "top_p", torch.float32, B, dev),
+        _ptr(min_p, "min_p", torch.float32, B, dev),
+        _ptr(uid, "uid", torch.int64, B, dev),
+        int(step) & ((1 << 64) - 1),
+        _ptr(tokens_out, "tokens_out", torch.int32, B, dev))
+    if code < 0:
+        raise SamplerError(code, "sample_batch_static", (load().sampler_last_error(None) or b"").decode())
     return tokens_out
 
 

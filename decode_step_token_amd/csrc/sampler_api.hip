@@ -13,6 +13,7 @@
 
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -34,6 +35,50 @@ constexpr int64_t kMaxGather = INT32_MAX;
 // all-greedy batches with at least this many rows fill the GPU with one
 // workgroup per row and take the single-pass kernel; smaller ones split rows
 constexpr int kStreamGreedyMinRows = 256;
+
+// Workspace of sample_batch_static, the entry point that allocates nothing:
+// the split-row kernel's records, candidate blocks, histograms, decision
+// words and flags for up to kStaticRows rows of up to kStaticChunks chunks
+// (fp32 rows up to 163840 entries, bf16 up to 327680).  One copy per GPU,
+// zero at load, held until the process ends; the host addresses it only
+// through the device address hipGetSymbolAddress returns for that GPU.
+constexpr int kStaticRows = 64;
+constexpr int kStaticChunks = 20;
+constexpr size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+constexpr size_t kStaticRecBytes = align256(sizeof(dst::SplitRec) * kStaticRows * kStaticChunks);
+constexpr size_t kStaticCandBytes =
+    align256(sizeof(uint64_t) * dst::kSplitCandStride * kStaticRows * kStaticChunks);
+constexpr size_t kStaticHistBytes = align256(sizeof(float) * dst::kSplitHistBins * kStaticRows * kStaticChunks);
+constexpr size_t kStaticDecBytes = align256(sizeof(uint32_t) * 4 * kStaticRows);
+constexpr size_t kStaticFlagBytes = align256(sizeof(uint32_t) * dst::kSplitMaxChunks * kStaticRows);
+constexpr size_t kStaticScratchBytes =
+    kStaticRecBytes + kStaticCandBytes + kStaticHistBytes + kStaticDecBytes + kStaticFlagBytes;
+constexpr int kStaticMaxDevices = 64;
+
+}  // namespace
+
+// sample_batch_static's workspace (see above): a kernel reaches it only
+// through the per-GPU device address kept in g_static.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+struct StaticDevice {
+    void* scratch = nullptr;    // device address of this GPU's copy (null: not set up yet)
+    uint32_t epoch = 0;         // last launch's publication epoch on it
+};
+StaticDevice g_static[kStaticMaxDevices];
+std::mutex g_static_mu;
+thread_local std::string g_static_error;
+
+int static_fail(int code, const char* msg, hipError_t he = hipSuccess) {
+    g_static_error = msg;
+    if (he != hipSuccess) {
+        g_static_error += ": ";
+        g_static_error += hipGetErrorString(he);
+    }
+    return code;
+}
 
 struct DeviceGuard {
     int prev = -1;
@@ -114,7 +159,7 @@ const char* sampler_strerror(int code) {
     }
 }
 
-const char* sampler_last_error(dst_sampler* s) { return s ? s->last_error.c_str() : ""; }
+const char* sampler_last_error(dst_sampler* s) { return s ? s->last_error.c_str() : g_static_error.c_str(); }
 
 int sampler_destroy(dst_sampler* s) {
     if (!s) return SAMPLER_OK;
@@ -314,6 +359,77 @@ int sample_batch(dst_sampler* s, void* stream, const void* logits, int64_t row_s
         }
     }
     if (e != hipSuccess) return fail(s, SAMPLER_EHIP, "sample_batch: launch", e);
+    return SAMPLER_OK;
+}
+
+int sample_batch_static(int device, void* stream, const void* logits, int64_t row_stride, int32_t B,
+                        int32_t vocab_size, int32_t logits_dtype, uint64_t seed, const float* temperature,
+                        const int32_t* top_k, const float* top_p, const float* min_p, const int64_t* uid,
+                        uint64_t step, int32_t* tokens_out) {
+    if (device < 0 || device >= kStaticMaxDevices)
+        return static_fail(SAMPLER_EINVAL, "sample_batch_static: device out of range");
+    if (B < 0 || B > kStaticRows)
+        return static_fail(SAMPLER_EINVAL, "sample_batch_static: B outside 0 .. 64 (the static workspace)");
+    if (logits_dtype != SAMPLER_F32 && logits_dtype != SAMPLER_BF16)
+        return static_fail(SAMPLER_EINVAL, "sample_batch_static: unknown logits dtype");
+    if (vocab_size < 1) return static_fail(SAMPLER_EINVAL, "sample_batch_static: vocab_size < 1");
+    int chunks = 0;
+    const int nl = dst::split_plan(vocab_size, logits_dtype, &chunks);
+    if (!nl || chunks > kStaticChunks)
+        return static_fail(SAMPLER_EINVAL,
+                           "sample_batch_static: vocab_size beyond the static workspace "
+                           "(163840 fp32 / 327680 bf16 entries)");
+    if (row_stride < vocab_size) return static_fail(SAMPLER_EINVAL, "sample_batch_static: row_stride < vocab_size");
+    if (B == 0) return SAMPLER_OK;
+    if (!logits || !tokens_out) return static_fail(SAMPLER_EINVAL, "sample_batch_static: null logits or tokens_out");
+    if (temperature && !uid) return static_fail(SAMPLER_EINVAL, "sample_batch_static: uid required with temperature");
+    const int64_t esize = logits_dtype == SAMPLER_F32 ? 4 : 2;
+    if ((reinterpret_cast<uintptr_t>(logits) & 15u) != 0 || ((row_stride * esize) & 15) != 0)
+        return static_fail(SAMPLER_EINVAL, "sample_batch_static: logits and row starts must be 16-byte aligned");
+    DeviceGuard g(device);
+    char* base = nullptr;
+    uint32_t epoch = 0;
+    {
+        std::lock_guard<std::mutex> lock(g_static_mu);
+        StaticDevice& sd = g_static[device];
+        if (!sd.scratch) {
+            // once per GPU, with that GPU current: the device address of its copy
+            void* p = nullptr;
+            const hipError_t he = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (he != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return static_fail(SAMPLER_EHIP, "sample_batch_static: hipGetSymbolAddress", he);
+            }
+            sd.scratch = p;
+        }
+        sd.epoch = sd.epoch + 2u == 0u ? 2u : sd.epoch + 2u;
+        base = static_cast<char*>(sd.scratch);
+        epoch = sd.epoch;
+    }
+    dst::SampleArgs a{};
+    a.logits = logits;
+    a.row_stride = row_stride;
+    a.B = B;
+    a.V = vocab_size;
+    a.temperature = temperature;
+    a.top_k = top_k;
+    a.top_p = top_p;
+    a.min_p = min_p;
+    a.uid = uid;
+    a.step = step;
+    a.seed = seed;
+    a.tokens_out = tokens_out;
+    a.rec = reinterpret_cast<dst::SplitRec*>(base);
+    a.cand = reinterpret_cast<uint64_t*>(base + kStaticRecBytes);
+    a.hist = reinterpret_cast<float*>(base + kStaticRecBytes + kStaticCandBytes);
+    a.dec = reinterpret_cast<uint32_t*>(base + kStaticRecBytes + kStaticCandBytes + kStaticHistBytes);
+    a.flags = reinterpret_cast<uint32_t*>(base + kStaticRecBytes + kStaticCandBytes + kStaticHistBytes +
+                                          kStaticDecBytes);
+    a.rec_stride = kStaticChunks;
+    a.chunks = chunks;
+    a.epoch = epoch;
+    const hipError_t e = dst::launch_sample_split(a, logits_dtype, nl, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return static_fail(SAMPLER_EHIP, "sample_batch_static: launch", e);
     return SAMPLER_OK;
 }
 

@@ -168,6 +168,31 @@ DST_API int sample_batch(dst_sampler* s, void* stream, const void* logits, int64
                  int32_t* tokens_out, const sampler_debug* dbg);
 
 /*
+ * sample_batch_static -- sample_batch for callers that cannot allocate: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  No handle, no allocation of any kind: the split-row kernel's
+ * workspace is a file-scope device array (18.5 MB, one copy per GPU,
+ * held until the process ends), addressed through hipGetSymbolAddress on the
+ * first call on each GPU.  Arguments as sample_batch, plus:
+ *   device       HIP device ordinal the call runs on (made current for it).
+ *   vocab_size   V, 1 .. 163840 for SAMPLER_F32, 1 .. 327680 for SAMPLER_BF16.
+ *   logits_dtype SAMPLER_F32 or SAMPLER_BF16.
+ *   seed         key of the counter-based generator (as sampler_create's).
+ * B is limited to 0 .. 64; logits and every row start must be 16-byte
+ * aligned.  No debug outputs.  Calls on one GPU share its workspace: calls
+ * that overlap in time on one GPU (different streams, or threads) race and
+ * must be serialised by the caller; consecutive calls on one stream are
+ * safe.  Errors (synchronous, nothing enqueued): SAMPLER_EINVAL for sizes
+ * beyond those limits or bad arguments, SAMPLER_EHIP; the message is
+ * sampler_last_error(NULL) on the calling thread.
+ */
+DST_API int sample_batch_static(int device, void* stream, const void* logits, int64_t row_stride,
+                        int32_t B, int32_t vocab_size, int32_t logits_dtype, uint64_t seed,
+                        const float* temperature, const int32_t* top_k, const float* top_p,
+                        const float* min_p, const int64_t* uid, uint64_t step,
+                        int32_t* tokens_out);
+
+/*
  * write_tokens -- token_pool[rows[b], cols[b]] = tokens[b], then an async copy
  * of tokens to host_pinned_out and a completion event ("The scheduler skeleton
  * and the offline interface", sections "Preparing a batch" and "_forward";
@@ -315,7 +340,8 @@ DST_API int sampler_check(dst_sampler* s);
 /* sampler_strerror -- static string for a status code. */
 DST_API const char* sampler_strerror(int code);
 
-/* sampler_last_error -- detail of the handle's last failure ("" if none). */
+/* sampler_last_error -- detail of the handle's last failure ("" if none);
+ * NULL: of the calling thread's last failed sample_batch_static. */
 DST_API const char* sampler_last_error(dst_sampler* s);
 
 #ifdef __cplusplus
