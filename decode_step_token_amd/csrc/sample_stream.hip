@@ -98,7 +98,7 @@ struct Smem {
     float tref[kMaxTiles];
     double tsum[kMaxTiles];
     double tacc[kMaxTiles];       // per-tile counts / weights of the candidate tail
-    uint16_t tstart[kMaxTiles];   // a tile's first slot in its wave's region
+    uint16_t tstart[kMaxTiles];   // a tile's first slot (in the region of the wave that read it)
     uint16_t tcnt[kMaxTiles];     // ... and its number of entries
     alignas(16) uint32_t hcnt[kBins];
     alignas(16) double hmass[kBins];
@@ -133,6 +133,7 @@ struct Smem {
     float xw[kList];
     uint32_t xidx[kList];
     uint32_t cut_key, cut_last;
+    uint32_t next_tile;    // the stream's next unclaimed tile
 };
 
 // ------------------------------------------------------------ tile I/O --
@@ -696,7 +697,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                     base += cu_all;
                 }
                 if (lane == 0) {
-                    ss.tstart[t] = static_cast<uint16_t>(cnt);
+                    ss.tstart[t] = static_cast<uint16_t>(wid * kRegion + static_cast<int>(cnt));
                     ss.tcnt[t] = static_cast<uint16_t>(total);
                 }
             }
@@ -714,6 +715,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         ss.mtotal = 0u;
         ss.movf = 0u;
         ss.list_n = 0u;
+        ss.next_tile = 2 * kWaves;
     }
     if (want_cand) {
         if (threadIdx.x < kMaxTiles) {
@@ -827,12 +829,21 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         }
     }
     if (!use_row) {
+        // A wave's first two tiles are t and t + 16; after that each wave
+        // claims the next unread tile as it starts on one, so the waves that
+        // run ahead read more tiles and all finish close together.  Each
+        // wave's tiles still come in increasing order.
         if (t < n_tiles) process(raw, t);
-        for (t += kWaves; t < n_tiles; t += kWaves) {
+        int tn = t + kWaves;          // the tile in nxt
+        while (tn < n_tiles) {
+            const int tc = tn;
 #pragma unroll
             for (int v = 0; v < IO::U; ++v) raw[v] = nxt[v];
-            if (t + kWaves < n_tiles) IO::load(row, V, t + kWaves, lane, nxt);
-            process(raw, t);
+            uint32_t cl = 0;
+            if (lane == 0) cl = atomicAdd(&ss.next_tile, 1u);
+            tn = __builtin_amdgcn_readfirstlane(static_cast<int>(cl));
+            if (tn < n_tiles) IO::load(row, V, tn, lane, nxt);
+            process(raw, tc);
         }
     } else {
         // the re-reading path needs the maximum first
@@ -1443,7 +1454,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 }
                 ts = static_cast<int>(readlane_u32(static_cast<uint32_t>(ts), owner));
                 rem = readlane_f64(rem, owner);
-                const int sb = (ts & (kWaves - 1)) * kRegion + ss.tstart[ts];
+                const int sb = ss.tstart[ts];
                 const int n = ss.tcnt[ts];
                 const Cut rcut = rc;
                 double run = 0.0;
@@ -1747,7 +1758,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 if (ts < 0) ts = last_t;        // rounding: u * W at or past the total
                 uint32_t found = 0xffffffffu, last = 0xffffffffu;
                 if (ts >= 0) {
-                    const int sb = (ts & (kWaves - 1)) * kRegion + ss.tstart[ts];
+                    const int sb = ss.tstart[ts];
                     const int n = ss.tcnt[ts];
                     double run2 = 0.0;
                     for (int j0 = 0; j0 < n; j0 += kWave) {
