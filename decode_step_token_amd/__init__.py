@@ -8,15 +8,16 @@ sampling parameters are prepared from host arrays and a step's new KV pages
 are written into the page table.  See ``include/sampler.h`` for the C ABI; this package is its
 ctypes binding.
 """
-from ._binding import (EXPORTS, LIB_PATH, SAMPLER_BF16, SAMPLER_DEBUG_TOPK, SAMPLER_F32, Sampler,
+from ._binding import (EXPORTS, LIB_PATH, SAMPLER_BF16, SAMPLER_CHECK_DUPLICATE_ROWS, SAMPLER_DEBUG_TOPK,
+                       SAMPLER_F32, Sampler,
                        SamplerArgs, SamplerDebug, SamplerError, gather_tokens, load, sample_batch,
                        sample_batch_static, sampler_check, sampler_create, sampler_destroy, sampler_prepare,
-                       sampler_query, sampler_strerror, sampler_wait, write_page_table,
+                       sampler_query, sampler_set_checks, sampler_strerror, sampler_wait, write_page_table,
                        write_tokens)
 
 __all__ = [
-    "EXPORTS", "LIB_PATH", "SAMPLER_BF16", "SAMPLER_DEBUG_TOPK", "SAMPLER_F32", "Sampler",
+    "EXPORTS", "LIB_PATH", "SAMPLER_BF16", "SAMPLER_CHECK_DUPLICATE_ROWS", "SAMPLER_DEBUG_TOPK", "SAMPLER_F32", "Sampler",
     "SamplerArgs", "SamplerDebug", "SamplerError", "gather_tokens", "load", "sample_batch",
     "sample_batch_static", "sampler_check", "sampler_create", "sampler_destroy", "sampler_prepare", "sampler_query",
-    "sampler_strerror", "sampler_wait", "write_page_table", "write_tokens",
+    "sampler_set_checks", "sampler_strerror", "sampler_wait", "write_page_table", "write_tokens",
 ]

@@ -32,7 +32,7 @@ STATUS = {0: "SAMPLER_OK", -1: "SAMPLER_EINVAL", -2: "SAMPLER_ENOMEM", -3: "SAMP
 EXPORTS = ("sampler_create", "sampler_destroy", "sampler_prepare", "sample_batch",
            "sample_batch_static", "write_tokens",
            "gather_tokens", "write_page_table", "sampler_wait", "sampler_query", "sampler_check",
-           "sampler_strerror", "sampler_last_error")
+           "sampler_strerror", "sampler_last_error", "sampler_set_checks")
 
 PREP_BYTES_PER_REQUEST = 24     # SAMPLER_PREP_BYTES(B) / B
 PREP_SLOTS = 8
@@ -57,6 +57,9 @@ class SamplerArgs(ctypes.Structure):
 
 
 _lib: Optional[ctypes.CDLL] = None
+# what each live handle was created with (handle value -> (dtype, vocab_size,
+# max_batch)), so that calls can be checked before any pointer crosses
+_HANDLES = {}
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -81,13 +84,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sampler_wait.argtypes = [P, U64]
     lib.sampler_query.argtypes = [P, U64]
     lib.sampler_check.argtypes = [P]
+    lib.sampler_set_checks.argtypes = [P, ctypes.c_uint32]
     lib.sampler_strerror.argtypes = [INT]
     lib.sampler_strerror.restype = ctypes.c_char_p
     lib.sampler_last_error.argtypes = [P]
     lib.sampler_last_error.restype = ctypes.c_char_p
     for name in ("sampler_create", "sampler_destroy", "sampler_prepare", "sample_batch",
                  "sample_batch_static", "write_tokens", "gather_tokens", "write_page_table", "sampler_wait",
-                 "sampler_query", "sampler_check"):
+                 "sampler_query", "sampler_check", "sampler_set_checks"):
         getattr(lib, name).restype = INT
     _lib = lib
     return lib
@@ -130,16 +134,56 @@ def sampler_create(device: int, max_batch: int, vocab_size: int, dtype: str = "f
                    seed: int = 42) -> ctypes.c_void_p:
     lib = load()
     h = ctypes.c_void_p()
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
     code = lib.sampler_create(ctypes.byref(h), int(device), int(max_batch), int(vocab_size),
                               SAMPLER_F32 if dtype == "f32" else SAMPLER_BF16,
                               int(seed) & ((1 << 64) - 1))
     _check(code, "sampler_create")
+    _HANDLES[h.value] = (dtype, int(vocab_size), int(max_batch))
     return h
 
 
 def sampler_destroy(handle) -> None:
     if handle:
+        _HANDLES.pop(handle.value if isinstance(handle, ctypes.c_void_p) else handle, None)
         _check(load().sampler_destroy(handle), "sampler_destroy")
+
+
+_LOGITS_DTYPES = {"f32": (torch.float32,), "bf16": (torch.bfloat16, torch.int16, torch.uint16)}
+
+
+def _check_batch_shapes(handle, logits: torch.Tensor, B: int, stride: int, tokens_out, debug) -> None:
+    """Sizes the kernels will read and write, checked against the tensors
+    before the call: a mismatch raises here instead of reaching past an
+    allocation on the device."""
+    key = handle.value if isinstance(handle, ctypes.c_void_p) else handle
+    meta = _HANDLES.get(key)
+    if B < 0 or B > logits.shape[0]:
+        raise ValueError(f"B={B} outside 0 .. {logits.shape[0]} (the rows of logits)")
+    if meta is not None:
+        dtype, V, max_batch = meta
+        if logits.dtype not in _LOGITS_DTYPES[dtype]:
+            raise TypeError(f"logits: the handle reads {dtype} rows, got a {logits.dtype} tensor")
+        if logits.shape[1] < V:
+            raise ValueError(f"logits rows hold {logits.shape[1]} < vocab_size {V} entries")
+        if B > max_batch:
+            raise ValueError(f"B={B} above the handle's max_batch {max_batch}")
+        if B > 0 and stride < V:
+            raise ValueError(f"row_stride {stride} < vocab_size {V}")
+        if B > 0 and (B - 1) * stride + V > logits.shape[0] * logits.stride(0):
+            raise ValueError("row_stride reaches past the logits tensor")
+    else:
+        V = None
+    if tokens_out.numel() < B:
+        raise ValueError(f"tokens_out holds {tokens_out.numel()} < B={B} elements")
+    if debug:
+        need = {"probs_out": None if V is None else B * V, "kept_out": B,
+                "topk_idx_out": B * SAMPLER_DEBUG_TOPK, "rand_out": B}
+        for field, n in need.items():
+            t = debug.get(field)
+            if t is not None and n is not None and t.numel() < n:
+                raise ValueError(f"{field} holds {t.numel()} < {n} elements")
 
 
 def sample_batch(handle, logits: torch.Tensor, temperature=None, top_k=None, top_p=None,
@@ -157,6 +201,7 @@ def sample_batch(handle, logits: torch.Tensor, temperature=None, top_k=None, top
     stride = logits.stride(0) if row_stride is None else int(row_stride)
     if tokens_out is None:
         tokens_out = torch.empty(B, dtype=torch.int32, device=dev)
+    _check_batch_shapes(handle, logits, B, stride, tokens_out, debug)
     dbg = None
     if debug:
         dbg = SamplerDebug()
@@ -350,6 +395,13 @@ def sampler_check(handle) -> None:
     _check(load().sampler_check(handle), "sampler_check", handle)
 
 
+SAMPLER_CHECK_DUPLICATE_ROWS = 1
+
+
+def sampler_set_checks(handle, flags: int) -> None:
+    _check(load().sampler_set_checks(handle, int(flags)), "sampler_set_checks", handle)
+
+
 def sampler_strerror(code: int) -> str:
     return load().sampler_strerror(int(code)).decode()
 
@@ -390,6 +442,9 @@ class Sampler:
 
     def check(self) -> None:
         sampler_check(self.handle)
+
+    def set_checks(self, flags: int) -> None:
+        sampler_set_checks(self.handle, flags)
 
     def close(self) -> None:
         if self.handle:

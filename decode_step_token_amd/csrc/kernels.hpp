@@ -120,6 +120,10 @@ int split_plan(int V, int dtype, int* chunks);
 int split_chunks_alloc(int V, int dtype);
 hipError_t launch_sample_split(const SampleArgs& args, int dtype, int nl, hipStream_t stream);
 hipError_t launch_write_tokens(const WriteArgs& args, hipStream_t stream);
+// debug check: sets *dup_status to 1 when two requests b != b' with cols != -1
+// name the same pool row (O(B^2) comparisons)
+hipError_t launch_check_rows(const int64_t* rows, const int64_t* cols, int B, uint32_t* dup_status,
+                             hipStream_t stream);
 hipError_t launch_gather_tokens(const GatherArgs& args, hipStream_t stream);
 hipError_t launch_write_page_table(const PageTableArgs& args, int n_records, hipStream_t stream);
 // copies n 4-byte words from mapped pinned host memory (its device address)

@@ -57,7 +57,10 @@ __global__ __launch_bounds__(kPageBlock) void write_page_table_kernel(PageTableA
             bad = true;
         }
     }
-    if (bad) __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (bad) {
+        __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __threadfence_system();    // performed for the host before the completion event
+    }
 }
 
 }  // namespace

@@ -25,8 +25,11 @@ namespace {
 constexpr int kRing = 256;
 // Completion events only: what the host reads after a wait (the token copy,
 // the status word) is written by the kernels straight into host memory with
-// system-scope stores, so no cache write-back at system scope is needed when
-// an event completes -- and skipping it saves ~2 us of idle GPU per event.
+// system-scope stores, each followed in its thread by a system-scope release
+// fence, so those stores are performed before the dispatch ends and hence
+// before the event is signalled; the event needs no cache write-back at
+// system scope of its own -- and skipping it saves ~2 us of idle GPU per
+// event.
 constexpr unsigned kEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
 // page-table staging: (row, first position, positions, first page) per request
 constexpr size_t kPageRecordBytes = 4 * sizeof(int64_t);
@@ -114,7 +117,8 @@ struct dst_sampler {
     int split_nl = 0;                  // loads per thread and chunk (0: rows go to the exact kernel)
     int split_chunks = 0;              // chunks per row
     uint32_t epoch = 0;                // last launch's publication epoch
-    uint32_t* status_host = nullptr;  // pinned, mapped: device bounds-check flag
+    uint32_t* status_host = nullptr;  // pinned, mapped: [0] bounds-check flag, [1] duplicate rows
+    uint32_t checks = 0;               // SAMPLER_CHECK_* flags
     uint32_t* status_dev = nullptr;
     hipEvent_t ring[kRing] = {};
     uint64_t ring_ticket[kRing] = {};
@@ -246,10 +250,11 @@ int sampler_create(dst_sampler** out, int device, int32_t max_batch, int32_t voc
         s->flags = reinterpret_cast<uint32_t*>(ws + rec_bytes + cand_bytes + hist_bytes + dec_bytes);
         e = hipMemset(s->dec, 0, dec_bytes + flag_bytes);
     }
-    if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&s->status_host), sizeof(uint32_t),
+    if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&s->status_host), 2 * sizeof(uint32_t),
                                            hipHostMallocMapped);
     if (e == hipSuccess) {
-        *s->status_host = 0;
+        s->status_host[0] = 0;
+        s->status_host[1] = 0;
         e = hipHostGetDevicePointer(reinterpret_cast<void**>(&s->status_dev), s->status_host, 0);
     }
     for (int i = 0; e == hipSuccess && i < kRing; ++i)
@@ -457,8 +462,10 @@ int write_tokens(dst_sampler* s, void* stream, int32_t* token_pool, int64_t pool
     if (B > 0) {
         // one kernel: pool scatter plus the tokens stored straight into the
         // pinned buffer (system-scope stores), no separate copy
+        if (s->checks & SAMPLER_CHECK_DUPLICATE_ROWS)
+            e = dst::launch_check_rows(rows, cols, B, s->status_dev + 1, st);
         dst::WriteArgs a{token_pool, pool_rows, pool_cols, rows, cols, tokens, B, s->status_dev, host_dev};
-        e = dst::launch_write_tokens(a, st);
+        if (e == hipSuccess) e = dst::launch_write_tokens(a, st);
     }
     const uint64_t ticket = s->issued + 1;
     if (e == hipSuccess) e = hipEventRecord(s->ring[ticket % kRing], st);
@@ -614,6 +621,8 @@ int sampler_wait(dst_sampler* s, uint64_t ticket) {
     if (e != hipSuccess) return fail(s, SAMPLER_EHIP, "sampler_wait", e);
     if (__atomic_load_n(s->status_host, __ATOMIC_ACQUIRE) != 0)
         return fail(s, SAMPLER_EDEVICE, "token-pool index out of range");
+    if (__atomic_load_n(s->status_host + 1, __ATOMIC_ACQUIRE) != 0)
+        return fail(s, SAMPLER_EDEVICE, "write_tokens: two requests name the same pool row");
     return SAMPLER_OK;
 }
 
@@ -633,7 +642,17 @@ int sampler_check(dst_sampler* s) {
     const hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return fail(s, SAMPLER_EHIP, "sampler_check", e);
     const uint32_t flag = __atomic_exchange_n(s->status_host, 0u, __ATOMIC_ACQ_REL);
+    const uint32_t dup = __atomic_exchange_n(s->status_host + 1, 0u, __ATOMIC_ACQ_REL);
     if (flag) return fail(s, SAMPLER_EDEVICE, "token-pool index out of range");
+    if (dup) return fail(s, SAMPLER_EDEVICE, "write_tokens: two requests name the same pool row");
+    return SAMPLER_OK;
+}
+
+int sampler_set_checks(dst_sampler* s, uint32_t flags) {
+    if (!s) return SAMPLER_EINVAL;
+    if (flags & ~static_cast<uint32_t>(SAMPLER_CHECK_DUPLICATE_ROWS))
+        return fail(s, SAMPLER_EINVAL, "sampler_set_checks: unknown flag");
+    s->checks = flags;
     return SAMPLER_OK;
 }
 

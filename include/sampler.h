@@ -202,7 +202,8 @@ DST_API int sample_batch_static(int device, void* stream, const void* logits, in
  *               the last column.  Any other out-of-range (row, col) skips that
  *               write and raises the handle's device flag (reported by
  *               sampler_wait / sampler_check as SAMPLER_EDEVICE).  Rows within
- *               one call must be distinct (one pool row per request).
+ *               one call must be distinct (one pool row per request;
+ *               sampler_set_checks can verify it).
  *   tokens      dev [B] int32 (e.g. sample_batch's tokens_out).
  *   host_pinned_out  host [B] int32 page-locked (hipHostMalloc / torch
  *               pin_memory) or NULL (no host copy).  Must stay valid until the
@@ -334,8 +335,24 @@ DST_API int sampler_wait(dst_sampler* s, uint64_t ticket);
 DST_API int sampler_query(dst_sampler* s, uint64_t ticket);
 
 /* sampler_check -- waits for the whole device, returns SAMPLER_EDEVICE if a
- * device bounds check fired since the last check, and clears the flag. */
+ * device bounds check (or an enabled debug check) fired since the last check,
+ * and clears the flags. */
 DST_API int sampler_check(dst_sampler* s);
+
+/* sampler_set_checks flags. */
+#define SAMPLER_CHECK_DUPLICATE_ROWS 1u
+
+/*
+ * sampler_set_checks -- debug checks for the handle's later calls (0: none,
+ * the default).  SAMPLER_CHECK_DUPLICATE_ROWS: before each write_tokens, a
+ * kernel compares every pair of requests that write (cols != -1) and raises
+ * the handle's device flag if two name the same pool row -- each request owns
+ * one row of the pool ("The scheduler skeleton and the offline interface",
+ * section "Preparing a batch").  Reported by sampler_wait / sampler_check as
+ * SAMPLER_EDEVICE; costs O(B^2) comparisons per call.  Errors: SAMPLER_EINVAL
+ * for an unknown flag.
+ */
+DST_API int sampler_set_checks(dst_sampler* s, uint32_t flags);
 
 /* sampler_strerror -- static string for a status code. */
 DST_API const char* sampler_strerror(int code);

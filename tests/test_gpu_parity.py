@@ -275,6 +275,25 @@ def test_write_tokens_errors_and_tickets():
     with pytest.raises(dst.SamplerError) as e:
         s.wait(10 ** 6)
     assert e.value.code == -6
+    # debug check: two requests on one pool row (cols -1 do not count)
+    s.set_checks(dst.SAMPLER_CHECK_DUPLICATE_ROWS)
+    t3 = s.write(pool, torch.tensor([0, 1, 1], dtype=torch.int64, device="cuda"),
+                 torch.tensor([2, -1, 4], dtype=torch.int64, device="cuda"), toks)
+    s.wait(t3)
+    t4 = s.write(pool, torch.tensor([3, 1, 3], dtype=torch.int64, device="cuda"),
+                 torch.tensor([2, 5, 4], dtype=torch.int64, device="cuda"), toks)
+    with pytest.raises(dst.SamplerError, match="same pool row") as e:
+        s.wait(t4)
+    assert e.value.code == -5
+    with pytest.raises(dst.SamplerError):
+        s.check()
+    s.check()  # cleared
+    s.set_checks(0)
+    t5 = s.write(pool, torch.tensor([3, 1, 3], dtype=torch.int64, device="cuda"),
+                 torch.tensor([2, 5, 4], dtype=torch.int64, device="cuda"), toks)
+    s.wait(t5)                                        # unchecked: no flag
+    with pytest.raises(dst.SamplerError):
+        s.set_checks(8)
     s.close()
 
 
@@ -282,14 +301,25 @@ def test_argument_errors():
     log("case argument errors")
     s = dst.Sampler(0, 4, 100, "f32")
     x = torch.zeros((5, 100), device="cuda")
-    with pytest.raises(dst.SamplerError) as e:
-        s.sample(x)                                   # B > max_batch
-    assert e.value.code == -1
+    with pytest.raises(ValueError, match="max_batch"):
+        s.sample(x)                                   # B > max_batch: the binding refuses it
+    # ... and so does the library itself, called through the C ABI directly
+    import ctypes
+    code = dst.load().sample_batch(s.handle, None, ctypes.c_void_p(x.data_ptr()), 100, 5,
+                                   None, None, None, None, None, 0,
+                                   ctypes.c_void_p(torch.empty(5, dtype=torch.int32, device="cuda").data_ptr()),
+                                   None)
+    assert code == -1
     y = torch.zeros((2, 100), device="cuda")
     with pytest.raises(dst.SamplerError):
         s.sample(y, temperature=torch.ones(2, device="cuda"))   # uid missing
-    with pytest.raises(dst.SamplerError):
+    with pytest.raises(ValueError, match="row_stride"):
         s.sample(y, row_stride=50)
+    code = dst.load().sample_batch(s.handle, None, ctypes.c_void_p(y.data_ptr()), 50, 2,
+                                   None, None, None, None, None, 0,
+                                   ctypes.c_void_p(torch.empty(2, dtype=torch.int32, device="cuda").data_ptr()),
+                                   None)
+    assert code == -1
     out = s.sample(y[:0])                             # B == 0 is a no-op
     assert out.numel() == 0
     s.close()
