@@ -18,6 +18,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdst_sampler.so")
+# the library's sources with AddressSanitizer and UndefinedBehaviorSanitizer
+# on the host side only, linked into a driver program (csrc/host_check.cpp)
+HOST_CHECK = os.path.join(LIBDIR, "host_check")
+SAN_BUILD = os.path.join(PKG, "_build", "host_san")
 
 SOURCES = ["sample_stream.hip", "sample_split.hip", "sample_exact.hip", "argmax.hip",
            "write_tokens.hip", "prepare.hip", "page_table.hip", "sampler_api.hip"]
@@ -32,6 +36,10 @@ CFLAGS = [
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 LDFLAGS = ["-shared", f"--offload-arch={ARCH}", "-Wl,-rpath,/opt/rocm/lib"]
+# every sanitizer flag is host-only (-Xarch_host): the device code is built
+# exactly as in the library
+HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 
 def _run(cmd, verbose):
@@ -46,22 +54,38 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every source and link the shared library; returns its path."""
+def build(verbose: bool = False, jobs: int | None = None, host_check: bool = True) -> str:
+    """Compile every source and link the shared library (and, with
+    host_check, the host-sanitized driver program); returns the library's
+    path."""
     os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(SAN_BUILD, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
-    objs = []
+    objs, san_objs = [], []
     cmds = []
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
-    jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 2) // 2), 8)
+    if host_check:
+        for src in SOURCES + ["host_check.cpp"]:
+            obj = os.path.join(SAN_BUILD, os.path.splitext(src)[0] + ".o")
+            san_objs.append(obj)
+            lang = ["-x", "hip"] if src.endswith(".cpp") else []
+            cmds.append([HIPCC, *CFLAGS, *HOST_SAN, "-g", *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+    # the two largest sources first
+    cmds.sort(key=lambda c: 0 if any(n in c[-3] for n in ("sample_stream", "sample_split")) else 1)
+    jobs = jobs or min(len(cmds), max(1, os.cpu_count() or 2), 16)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
     _run([HIPCC, *LDFLAGS, *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    if host_check:
+        tmp = HOST_CHECK + ".tmp"
+        _run([HIPCC, *HOST_SAN, f"--offload-arch={ARCH}", *san_objs, "-o", tmp, "-Wl,-rpath,/opt/rocm/lib"],
+             verbose)
+        os.replace(tmp, HOST_CHECK)
     return LIB
 
 

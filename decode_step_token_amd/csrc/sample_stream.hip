@@ -1319,6 +1319,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     uint32_t n_kept = 0, token = 0;
     double W = 0.0;
     bool fast = false;
+    bool cand_weights = false;    // the draw summed the candidates' fp32 weights
 
     // ------------------------------------------------------ candidate tail --
     // Passes over the candidates in the wave regions; after each pass wave 0
@@ -1921,6 +1922,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             }
             if (route == 1 || route == 2 || route == 4) {
                 fast = true;
+                cand_weights = true;
                 cut = Cut{ss.cut_key, ss.cut_last};
                 token = ss.res_token;
                 n_kept = ss.res_kept;
@@ -1949,6 +1951,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             }
             if (pd.type == kPassDone) {
                 fast = true;
+                cand_weights = true;
                 cut = Cut{pd.rkey, pd.rlast};
                 token = ss.res_token;
                 n_kept = ss.res_kept;
@@ -2277,11 +2280,16 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         if (a.rand_out) a.rand_out[b] = word;
     }
     if (a.probs_out) {
+        // each kept token's weight as the draw summed it (over the same W):
+        // the candidate routes' fp32 weights, or the row reads' fp32 exp2
+        // times G
         float* probs = a.probs_out + static_cast<int64_t>(b) * V;
         for (int i = threadIdx.x; i < V; i += kBlock) {
             const float x = Elem<DT>::at(row, i);
-            probs[i] = cut.keep(static_cast<uint32_t>(i), f32_key(x))
-                           ? static_cast<float>(fast_weight(x, mc, c) / W) : 0.0f;
+            const double wt = cand_weights
+                ? static_cast<double>(static_cast<float>(fast_weight(x, mc, c)))
+                : static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, c32, -Pf))) * G;
+            probs[i] = cut.keep(static_cast<uint32_t>(i), f32_key(x)) ? static_cast<float>(wt / W) : 0.0f;
         }
     }
     if (topk_out) {

@@ -201,7 +201,8 @@ def test_c3_full():
     _check(wl.c3(), probs_rows=set(range(0, 256, 13)))
 
 
-@pytest.mark.parametrize("step,half_greedy", [(0, False), (1, False), (63, False), (0, True)])
+@pytest.mark.parametrize("step,half_greedy", [(0, False), (1, False), (63, False), (0, True), (31, True),
+                                               (63, True)])
 def test_c4_decode_steps(step, half_greedy):
     _check(wl.c4(step, half_greedy), probs_rows=set(range(0, 512, 61)))
 
