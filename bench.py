@@ -103,8 +103,18 @@ def write_traffic(fetch_csv: str, write_csv: str, kernel: str, workload: str, co
 
     kname, kf, nf = pick(fetch, "sample_stream_kernel")
     _, kw, nw = pick(write, "sample_stream_kernel")
-    cname, cf, _ = pick(fetch, COPY_KERNEL_NEEDLE)
-    _, cw, _ = pick(write, COPY_KERNEL_NEEDLE)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    if any(COPY_KERNEL_NEEDLE in n for n in fetch):
+        cname, cf, _ = pick(fetch, COPY_KERNEL_NEEDLE)
+        _, cw, _ = pick(write, COPY_KERNEL_NEEDLE)
+    else:
+        # no copy kernel in these runs: the calibration of the c3 record
+        ref = data["sample_batch@c3"]
+        cname, cf, cw = ref["copy_kernel"], ref["copy_fetch_kib"], ref["copy_write_kib"]
     fscale = cf * 1024.0 / COPY_BYTES
     wscale = cw * 1024.0 / COPY_BYTES
     rec = {
@@ -119,11 +129,6 @@ def write_traffic(fetch_csv: str, write_csv: str, kernel: str, workload: str, co
         "sources_digest": kernel_sources_digest(),
         "command": command,
     }
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    data = {}
-    if os.path.exists(path):
-        with open(path) as f:
-            data = json.load(f)
     data[f"{kernel}@{workload}"] = rec
     with open(path, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
@@ -137,6 +142,41 @@ def _oracle_rows(task):
     logits, dtype, T, k, p, mp, uid, step, seed = task
     oracle.sample_batch(logits, dtype, T, k, p, uid, step, seed, min_p=mp)
     return len(uid)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_single_process(w, seconds: float) -> float:
+    """The oracle in this process, one row after another, for about
+    ``seconds``: rows per second on one core."""
+    import oracle
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        b = n % w.B
+        sl = lambda a: None if a is None else a[b:b + 1]
+        oracle.sample_batch(w.logits[b:b + 1], w.dtype, sl(w.temperature), sl(w.top_k), sl(w.top_p),
+                            w.uid[b:b + 1], w.step, w.seed, min_p=sl(w.min_p))
+        n += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    return n / (time.perf_counter() - t0)
+
+
+def percentiles_us(vals_ms):
+    import numpy as np
+    v = np.asarray(vals_ms) * 1e3
+    return {"mean": float(v.mean()), "median": float(np.median(v)), "p10": float(np.percentile(v, 10)),
+            "p90": float(np.percentile(v, 90))}
 
 
 def cpu_baseline(w, seconds: float):
@@ -167,9 +207,11 @@ def cpu_baseline(w, seconds: float):
             if time.perf_counter() - t0 > seconds:
                 break
         dt = time.perf_counter() - t0
+    single = oracle_single_process(w, min(5.0, seconds / 2))
     return {"value": n / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
             "sample": f"{passes} passes over the {w.B} rows of the same batch (steps s, s+1, ...), "
-                      f"fp64 NumPy oracle, {cores} worker processes, {per} rows per task"}
+                      f"fp64 NumPy oracle, {cores} worker processes, {per} rows per task",
+            "single_process_rows_per_s": single, "cpu_model": cpu_model()}
 
 
 def main():
@@ -186,14 +228,17 @@ def main():
                     help="record counter-measured bytes per launch in profiles/traffic.json")
     ap.add_argument("--traffic-command", default="",
                     help="with --write-traffic: the profiling command, stored with the figures")
-    ap.add_argument("--workload", choices=("c3", "c3minp", "c4loop"), default="c3",
+    ap.add_argument("--workload", choices=("c3", "c3minp", "c2", "c4loop"), default="c3",
                     help="c3: the headline sampler step (default); c3minp: the same batch with "
-                         "a per-request min_p; c4loop: the overlapped decode loop (prepare, page "
+                         "a per-request min_p; c2: B=256 V=128256 bf16, half greedy, half T=0.7 "
+                         "top-p 0.9; c4loop: the overlapped decode loop (prepare, page "
                          "table, gather, sample, write) at B=512 V=152064 bf16")
+    ap.add_argument("--traffic-workload", default="c3",
+                    help="with --write-traffic: the workload the counters were taken on")
     args = ap.parse_args()
 
     if args.write_traffic:
-        write_traffic(args.write_traffic[0], args.write_traffic[1], "sample_batch", "c3",
+        write_traffic(args.write_traffic[0], args.write_traffic[1], "sample_batch", args.traffic_workload,
                       args.traffic_command)
         return
 
@@ -212,8 +257,12 @@ def main():
     import decode_step_token_amd as dst
     import workloads as wl
 
-    eprint("bench: generating the B=256 V=151936 fp32 workload")
-    w = wl.c3()
+    if args.workload == "c2":
+        eprint("bench: generating the B=256 V=128256 bf16 workload")
+        w = wl.c2()
+    else:
+        eprint("bench: generating the B=256 V=151936 fp32 workload")
+        w = wl.c3()
     minp = None
     if args.workload == "c3minp":
         w = wl.with_min_p(w, C3_MIN_P_VALUES, 8)
@@ -221,18 +270,20 @@ def main():
     B, V = w.B, w.V
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    host_logits = torch.from_numpy(w.logits)
+    esize = 4 if w.dtype == "f32" else 2
+    host_logits = torch.from_numpy(w.logits if w.dtype == "f32" else w.logits.view(np.int16))
     bufs = [host_logits.to(dev) for _ in range(args.buffers)]
-    T = torch.from_numpy(w.temperature).to(dev)
-    k = torch.from_numpy(w.top_k).to(dev)
-    p = torch.from_numpy(w.top_p).to(dev)
+    opt = lambda a: None if a is None else torch.from_numpy(a).to(dev)
+    T = opt(w.temperature)
+    k = opt(w.top_k)
+    p = opt(w.top_p)
     uid = torch.from_numpy(w.uid).to(dev)
     pool = torch.from_numpy(w.pool.copy()).to(dev)
     rows = torch.from_numpy(w.rows).to(dev)
     cols0 = torch.from_numpy(w.cols).to(dev)
     tokens = torch.empty(B, dtype=torch.int32, device=dev)
     host_ring = [torch.empty(B, dtype=torch.int32).pin_memory() for _ in range(2)]
-    sampler = dst.Sampler(0, B, V, "f32", w.seed)
+    sampler = dst.Sampler(0, B, V, w.dtype, w.seed)
     stream = torch.cuda.current_stream()
 
     def step(s):
@@ -256,14 +307,18 @@ def main():
     eprint(f"bench: timing {args.steps} steps")
     t0 = time.perf_counter()
     prev = None
+    marks = []                      # host time at which each step's host copy is in
     for i in range(args.steps):
         t = step(args.warmup + i)
         if prev is not None:
             sampler.wait(prev)
+            marks.append(time.perf_counter())
         prev = t
     sampler.wait(prev)
+    marks.append(time.perf_counter())
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = [(b_ - a_) * 1e3 for a_, b_ in zip([t0] + marks[:-1], marks)]
 
     # timed region 2: the sample_batch kernel alone, the same launches back to
     # back, bracketed by two HIP events on the launch stream (an event pair
@@ -278,6 +333,19 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     kernel_ms_total = ev0.elapsed_time(ev1)
+    # timed region 3 (spread only): one event after every launch, so launch i
+    # spans the interval between events i and i + 1; each interval also holds
+    # the event between two launches, so these read a few us above the
+    # back-to-back average of region 2
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        sampler.sample(bufs[i % len(bufs)], temperature=T, top_k=k, top_p=p, uid=uid,
+                       step=args.warmup + 2 * args.steps + i, tokens_out=tokens, stream=stream,
+                       min_p=minp)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    launch_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     sampler.check()
     sampler.close()
 
@@ -291,19 +359,19 @@ def main():
 
     ms_per_step = elapsed * 1e3 / args.steps
     avg_kernel_ms = kernel_ms_total / args.steps
-    alg_bytes = B * (V * 4 + PARAM_BYTES_PER_ROW)
+    alg_bytes = B * (V * esize + PARAM_BYTES_PER_ROW)
     achieved = alg_bytes / (avg_kernel_ms * 1e-3) / 1e9
     eprint(f"bench: {ms_per_step * 1e3:.1f} us/step, sample_batch kernel avg "
            f"{avg_kernel_ms * 1e3:.1f} us, {achieved:.0f} GB/s")
 
-    traffic = load_traffic("sample_batch", "c3") if minp is None else None
+    traffic = load_traffic("sample_batch", args.workload) if args.workload in ("c3", "c2") else None
     cpu = None
     if not args.no_cpu_baseline:
         eprint(f"bench: timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
         cpu = cpu_baseline(w, args.cpu_seconds)
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload != "c2" else METRIC.replace("V=151936", f"V={V} bf16"),
         "value": B / (ms_per_step * 1e-3),
         "unit": "rows/s",
         "n_gpus": 1,
@@ -313,18 +381,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": "c3: B=256 V=151936 fp32 2*Gumbel+rank-4 logits, per-request "
-                               "T~U[0.3,1.5], top_k in {1,20,50,off}, top_p in {1,0.95,0.8}; "
-                               "token pool [256,4096]"
-                               + ("; min_p in {0,0.02,0.05,0.1}" if minp is not None else ""),
-                   "B": B, "V": V, "logits_dtype": "f32", "input_buffers": len(bufs),
+        "config": {"workload": ("c3: B=256 V=151936 fp32 2*Gumbel+rank-4 logits, per-request "
+                                "T~U[0.3,1.5], top_k in {1,20,50,off}, top_p in {1,0.95,0.8}; "
+                                "token pool [256,4096]"
+                                + ("; min_p in {0,0.02,0.05,0.1}" if minp is not None else ""))
+                   if args.workload != "c2" else
+                   "c2: B=256 V=128256 bf16 N(0,3) logits, even uids greedy, odd uids T=0.7 top-p 0.9",
+                   "B": B, "V": V, "logits_dtype": w.dtype, "input_buffers": len(bufs),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "sample_batch", "kernel_avg_us": avg_kernel_ms * 1e3,
-                     "alg_bytes_per_launch": alg_bytes},
+                     "alg_bytes_per_launch": alg_bytes,
+                     "event_interval_us": percentiles_us(launch_ms)},
+        "step_us": percentiles_us(step_ms),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
