@@ -1979,12 +1979,16 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) z += ss.wd[w];
         const double ztgt = static_cast<double>(prm.p) * z;
-        // bin index of a value (higher = heavier) and its exponent y, weight 2^y * G
-        auto depth_bin = [&](float x, float* y) -> int {
-            *y = fmaf(x, c32, -Pf);
-            const float dq = -*y * 16.0f;
-            const int bq = dq < 1.0f ? 0 : (dq >= static_cast<float>(kBins - 1) ? kBins - 1 : static_cast<int>(dq));
-            return kBins - 1 - bq;
+        // The weight of a value relative to the reference, 2^(x*c32 - Pf) (times
+        // G in fp64), and its bin: the weight's fp32 exponent and top four
+        // mantissa bits, so 16 bins per octave from 2^-64 up (higher bin =
+        // heavier); lighter weights and zero fall into bin 0, weights from
+        // about 0.97 up into the top bin.  Bin edges are bit patterns of the
+        // weight, so the second pass classifies a value with integer compares.
+        constexpr int kWBinBase = (127 - 64) << 4;
+        auto wbin = [&](float w) -> int {
+            const int q = static_cast<int>(__float_as_uint(w) >> 19) - kWBinBase;
+            return q < 0 ? 0 : (q > kBins - 1 ? kBins - 1 : q);
         };
         // pass A's histogram: kHistCopies adjacent copies of each bin, lane l
         // adding to copy l mod kHistCopies (so lanes of a wave seldom meet on one
@@ -2008,11 +2012,9 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 if (tt + kWaves < n_tiles) IO::load(row, V, tt + kWaves, lane, ra);
 #pragma unroll
                 for (int q = 0; q < Q; ++q) {
-                    if (IO::index(tt, lane, q) < static_cast<uint32_t>(V)) {
-                        float y;
-                        const int d = depth_bin(IO::get(rb, q), &y);
-                        atomicAdd(&hl[d * kHistCopies], static_cast<double>(__builtin_amdgcn_exp2f(y)));
-                    }
+                    // past the row's end the value is -inf: weight 0, bin 0
+                    const float w = __builtin_amdgcn_exp2f(fmaf(IO::get(rb, q), c32, -Pf));
+                    atomicAdd(&hl[wbin(w) * kHistCopies], static_cast<double>(w));
                 }
             }
         }
@@ -2037,6 +2039,10 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         }
         __syncthreads();
         const int dpick = static_cast<int>(ss.bu[2]);
+        // bit patterns of the weights in bin dpick: [wlo, whi) (zero weights,
+        // which no cut with p < 1 keeps, never count as inside)
+        const uint32_t wlo = dpick == 0 ? 1u : static_cast<uint32_t>(dpick + kWBinBase) << 19;
+        const uint32_t whi = dpick == kBins - 1 ? 0xffffffffu : static_cast<uint32_t>(dpick + 1 + kWBinBase) << 19;
         // (B)
         {
             uint4 ra[IO::U], rb[IO::U];
@@ -2048,34 +2054,32 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
 #pragma unroll
                 for (int v = 0; v < IO::U; ++v) rb[v] = ra[v];
                 if (tt + kWaves < n_tiles) IO::load(row, V, tt + kWaves, lane, ra);
-                double part = 0.0;
+                // the lane's weights above the bin: at most Q of them, summed
+                // in fp32 (relative error below Q * 2^-24), then in fp64
+                float part = 0.0f;
 #pragma unroll
                 for (int q = 0; q < Q; ++q) {
                     const float x = IO::get(rb, q);
-                    const uint32_t idx = IO::index(tt, lane, q);
-                    float y;
-                    const int d = depth_bin(x, &y);
-                    const bool valid = idx < static_cast<uint32_t>(V);
-                    const float w = __builtin_amdgcn_exp2f(y);
-                    if (valid && d > dpick) {
-                        part += static_cast<double>(w);
-                        ++nabove;
-                    }
-                    const uint64_t bal = __ballot(valid && d == dpick);
+                    const float w = __builtin_amdgcn_exp2f(fmaf(x, c32, -Pf));
+                    const uint32_t wb = __float_as_uint(w);
+                    const bool up = wb >= whi;
+                    part += up ? w : 0.0f;
+                    nabove += static_cast<uint32_t>(__popcll(__ballot(up)));
+                    const bool inb = wb >= wlo && wb < whi;
+                    const uint64_t bal = __ballot(inb);
                     if (bal) {
                         const uint32_t pos = fill + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u));
-                        if (valid && d == dpick && pos < static_cast<uint32_t>(kRegion)) {
-                            ss.cent[rbeg + pos] = make_uint2(f32_key(x), idx);
+                        if (inb && pos < static_cast<uint32_t>(kRegion)) {
+                            ss.cent[rbeg + pos] = make_uint2(f32_key(x), IO::index(tt, lane, q));
                             ss.cw[rbeg + pos] = static_cast<float>(static_cast<double>(w) * G);
                         }
                         fill += static_cast<uint32_t>(__popcll(bal));
                     }
                 }
-                const double ts = wave_sum_dpp(part);
+                const double ts = wave_sum_dpp(static_cast<double>(part));
                 if (lane == 0) ss.tacc[tt] = ts * G;
             }
-            nabove = readlane_u32(wave_scan_u32_dpp(nabove), kWave - 1);
             if (lane == 0) {
                 if (fill > static_cast<uint32_t>(kRegion)) atomicOr(&ss.movf, 1u);
                 atomicAdd(&ss.mtotal, nabove);
