@@ -1992,7 +1992,8 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         };
         // pass A's histogram: kHistCopies adjacent copies of each bin, lane l
         // adding to copy l mod kHistCopies (so lanes of a wave seldom meet on one
-        // address), kept in the candidate regions, which pass B refills
+        // address), kept in the candidate regions, which pass B refills (fp64:
+        // LDS fp32 atomic adds run an order of magnitude slower here)
         constexpr int kHistCopies = 8;
         static_assert(sizeof(double) * kBins * kHistCopies <= sizeof(ss.cent), "histogram copies fit");
         double* const hist = reinterpret_cast<double*>(ss.cent);
@@ -2055,31 +2056,43 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 for (int v = 0; v < IO::U; ++v) rb[v] = ra[v];
                 if (tt + kWaves < n_tiles) IO::load(row, V, tt + kWaves, lane, ra);
                 // the lane's weights above the bin: at most Q of them, summed
-                // in fp32 (relative error below Q * 2^-24), then in fp64
+                // in fp32 (relative error below Q * 2^-24), then in fp64; its
+                // entries inside the bin as a bit mask, stored after one scan
+                // of the lanes' counts
                 float part = 0.0f;
+                float wq[Q];
+                uint32_t inm = 0u;
 #pragma unroll
                 for (int q = 0; q < Q; ++q) {
-                    const float x = IO::get(rb, q);
-                    const float w = __builtin_amdgcn_exp2f(fmaf(x, c32, -Pf));
+                    const float w = __builtin_amdgcn_exp2f(fmaf(IO::get(rb, q), c32, -Pf));
+                    wq[q] = w;
                     const uint32_t wb = __float_as_uint(w);
                     const bool up = wb >= whi;
                     part += up ? w : 0.0f;
-                    nabove += static_cast<uint32_t>(__popcll(__ballot(up)));
-                    const bool inb = wb >= wlo && wb < whi;
-                    const uint64_t bal = __ballot(inb);
-                    if (bal) {
-                        const uint32_t pos = fill + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u));
-                        if (inb && pos < static_cast<uint32_t>(kRegion)) {
-                            ss.cent[rbeg + pos] = make_uint2(f32_key(x), IO::index(tt, lane, q));
-                            ss.cw[rbeg + pos] = static_cast<float>(static_cast<double>(w) * G);
+                    nabove += up ? 1u : 0u;
+                    inm |= (wb >= wlo && wb < whi ? 1u : 0u) << q;
+                }
+                const uint32_t ln = static_cast<uint32_t>(__popc(inm));
+                const uint32_t incl = wave_scan_u32_dpp(ln);
+                const uint32_t tot = readlane_u32(incl, kWave - 1);
+                if (tot != 0u) {
+                    uint32_t pos = fill + incl - ln;
+#pragma unroll
+                    for (int q = 0; q < Q; ++q) {
+                        if ((inm >> q) & 1u) {
+                            if (pos < static_cast<uint32_t>(kRegion)) {
+                                ss.cent[rbeg + pos] = make_uint2(f32_key(IO::get(rb, q)), IO::index(tt, lane, q));
+                                ss.cw[rbeg + pos] = static_cast<float>(static_cast<double>(wq[q]) * G);
+                            }
+                            ++pos;
                         }
-                        fill += static_cast<uint32_t>(__popcll(bal));
                     }
+                    fill += tot;
                 }
                 const double ts = wave_sum_dpp(static_cast<double>(part));
                 if (lane == 0) ss.tacc[tt] = ts * G;
             }
+            nabove = readlane_u32(wave_scan_u32_dpp(nabove), kWave - 1);
             if (lane == 0) {
                 if (fill > static_cast<uint32_t>(kRegion)) atomicOr(&ss.movf, 1u);
                 atomicAdd(&ss.mtotal, nabove);
@@ -2102,98 +2115,96 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             Cut pc{0u, 0xffffffffu};
             double wb = 0.0;
             uint32_t nb = 0;
-            if (!mass_cut(Cut{0u, 0xffffffffu}, ztgt - above, &pc, &wb, &nb)) {
-                // rounding: the target is at or past the bin's end; keep it whole
-                uint32_t lo, hi;
-                key_range(Cut{0u, 0xffffffffu}, &lo, &hi);
-                pc = Cut{lo, 0xffffffffu};
-                wb = sum_cut(pc, &nb);
-            }
-            cut = pc;
-            W = above + wb;
-            n_kept = nabove + nb;
-            // the kept entries of the bin add their weight to their tile
-            each(0u, 0xffffffffu, [&](uint32_t k, uint32_t i, int slot) {
-                if (cut.keep(i, k)) atomicAdd(&ss.tacc[i >> kTS], static_cast<double>(ss.cw[slot]));
-            });
-            __syncthreads();
-            if (wid == 0) {
-                // the tile holding u * W (lane l: tiles l*per ..), then that tile again
-                const int per = (n_tiles + kWave - 1) / kWave;
-                const int tlo = lane * per, thi = tlo + per < n_tiles ? tlo + per : n_tiles;
-                double psum = 0.0;
-                for (int i = tlo; i < thi; ++i) psum += ss.tacc[i];
-                const double incl = wave_scan_f64_dpp(psum);
-                const double tot = readlane_f64(incl, kWave - 1);
-                const double target = u * tot;
-                const uint64_t bal = __ballot(psum > 0.0 && incl > target);
-                const uint64_t nz = __ballot(psum > 0.0);
-                const int owner = bal ? __ffsll(static_cast<unsigned long long>(bal)) - 1
-                                      : (nz ? 63 - __clzll(static_cast<long long>(nz)) : 0);
-                int ts = tlo;
-                double rem = INFINITY;
-                if (lane == owner) {
-                    double cum = incl - psum;
-                    int found = -1, last_nz = tlo;
-                    for (int i = tlo; i < thi; ++i) {
-                        const double v = ss.tacc[i];
-                        if (v > 0.0) last_nz = i;
-                        if (found < 0 && v > 0.0 && cum + v > target) { found = i; rem = target - cum; }
-                        if (found < 0) cum += v;
-                    }
-                    ts = found >= 0 ? found : last_nz;
-                    if (found < 0) rem = INFINITY;
-                }
-                ts = static_cast<int>(readlane_u32(static_cast<uint32_t>(ts), owner));
-                rem = readlane_f64(rem, owner);
-                uint4 rr[IO::U];
-                IO::load(row, V, ts, lane, rr);
-                double run = 0.0;
-                int tok = -1, last_pos = -1;
-#pragma unroll
-                for (int uu = 0; uu < IO::U; ++uu) {
-                    double wv[IO::VEC];
-                    double ps = 0.0;
-                    int my_last = -1;
-#pragma unroll
-                    for (int e = 0; e < IO::VEC; ++e) {
-                        const float x = IO::get(rr, uu * IO::VEC + e);
-                        const uint32_t idx = IO::index(ts, lane, uu * IO::VEC + e);
-                        const bool kp = idx < static_cast<uint32_t>(V) && cut.keep(idx, f32_key(x));
-                        wv[e] = kp ? static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, c32, -Pf))) * G : 0.0;
-                        ps += wv[e];
-                        if (wv[e] > 0.0) my_last = static_cast<int>(idx);
-                    }
-                    const double pin = wave_scan_f64_dpp(ps);
-                    const double tsum = readlane_f64(pin, kWave - 1);
-                    const uint64_t lastb = __ballot(my_last >= 0);
-                    if (lastb)
-                        last_pos = static_cast<int>(readlane_u32(static_cast<uint32_t>(my_last),
-                                                                 63 - __clzll(static_cast<long long>(lastb))));
-                    if (tok < 0 && run + tsum > rem) {
-                        const uint64_t ob = __ballot(ps > 0.0 && run + pin > rem);
-                        if (ob) {
-                            const int own = __ffsll(static_cast<unsigned long long>(ob)) - 1;
-                            int mine = -1;
-                            bool done_l = false;
-                            double cum = run + (pin - ps);
-#pragma unroll
-                            for (int e = 0; e < IO::VEC; ++e) {
-                                cum += wv[e];
-                                if (!done_l && wv[e] > 0.0) mine = static_cast<int>(IO::index(ts, lane, uu * IO::VEC + e));
-                                if (wv[e] > 0.0 && cum > rem) done_l = true;
-                            }
-                            tok = static_cast<int>(readlane_u32(static_cast<uint32_t>(mine), own));
+            // the target must fall inside the bin pass A picked; a target that
+            // rounding of the two passes' sums puts on the other side of a bin
+            // edge leaves the row to the row path
+            if (ztgt > above && mass_cut(Cut{0u, 0xffffffffu}, ztgt - above, &pc, &wb, &nb)) {
+                cut = pc;
+                W = above + wb;
+                n_kept = nabove + nb;
+                // the kept entries of the bin add their weight to their tile
+                each(0u, 0xffffffffu, [&](uint32_t k, uint32_t i, int slot) {
+                    if (cut.keep(i, k)) atomicAdd(&ss.tacc[i >> kTS], static_cast<double>(ss.cw[slot]));
+                });
+                __syncthreads();
+                if (wid == 0) {
+                    // the tile holding u * W (lane l: tiles l*per ..), then that tile again
+                    const int per = (n_tiles + kWave - 1) / kWave;
+                    const int tlo = lane * per, thi = tlo + per < n_tiles ? tlo + per : n_tiles;
+                    double psum = 0.0;
+                    for (int i = tlo; i < thi; ++i) psum += ss.tacc[i];
+                    const double incl = wave_scan_f64_dpp(psum);
+                    const double tot = readlane_f64(incl, kWave - 1);
+                    const double target = u * tot;
+                    const uint64_t bal = __ballot(psum > 0.0 && incl > target);
+                    const uint64_t nz = __ballot(psum > 0.0);
+                    const int owner = bal ? __ffsll(static_cast<unsigned long long>(bal)) - 1
+                                          : (nz ? 63 - __clzll(static_cast<long long>(nz)) : 0);
+                    int ts = tlo;
+                    double rem = INFINITY;
+                    if (lane == owner) {
+                        double cum = incl - psum;
+                        int found = -1, last_nz = tlo;
+                        for (int i = tlo; i < thi; ++i) {
+                            const double v = ss.tacc[i];
+                            if (v > 0.0) last_nz = i;
+                            if (found < 0 && v > 0.0 && cum + v > target) { found = i; rem = target - cum; }
+                            if (found < 0) cum += v;
                         }
+                        ts = found >= 0 ? found : last_nz;
+                        if (found < 0) rem = INFINITY;
                     }
-                    run += tsum;
+                    ts = static_cast<int>(readlane_u32(static_cast<uint32_t>(ts), owner));
+                    rem = readlane_f64(rem, owner);
+                    uint4 rr[IO::U];
+                    IO::load(row, V, ts, lane, rr);
+                    double run = 0.0;
+                    int tok = -1, last_pos = -1;
+    #pragma unroll
+                    for (int uu = 0; uu < IO::U; ++uu) {
+                        double wv[IO::VEC];
+                        double ps = 0.0;
+                        int my_last = -1;
+    #pragma unroll
+                        for (int e = 0; e < IO::VEC; ++e) {
+                            const float x = IO::get(rr, uu * IO::VEC + e);
+                            const uint32_t idx = IO::index(ts, lane, uu * IO::VEC + e);
+                            const bool kp = idx < static_cast<uint32_t>(V) && cut.keep(idx, f32_key(x));
+                            wv[e] = kp ? static_cast<double>(__builtin_amdgcn_exp2f(fmaf(x, c32, -Pf))) * G : 0.0;
+                            ps += wv[e];
+                            if (wv[e] > 0.0) my_last = static_cast<int>(idx);
+                        }
+                        const double pin = wave_scan_f64_dpp(ps);
+                        const double tsum = readlane_f64(pin, kWave - 1);
+                        const uint64_t lastb = __ballot(my_last >= 0);
+                        if (lastb)
+                            last_pos = static_cast<int>(readlane_u32(static_cast<uint32_t>(my_last),
+                                                                     63 - __clzll(static_cast<long long>(lastb))));
+                        if (tok < 0 && run + tsum > rem) {
+                            const uint64_t ob = __ballot(ps > 0.0 && run + pin > rem);
+                            if (ob) {
+                                const int own = __ffsll(static_cast<unsigned long long>(ob)) - 1;
+                                int mine = -1;
+                                bool done_l = false;
+                                double cum = run + (pin - ps);
+    #pragma unroll
+                                for (int e = 0; e < IO::VEC; ++e) {
+                                    cum += wv[e];
+                                    if (!done_l && wv[e] > 0.0) mine = static_cast<int>(IO::index(ts, lane, uu * IO::VEC + e));
+                                    if (wv[e] > 0.0 && cum > rem) done_l = true;
+                                }
+                                tok = static_cast<int>(readlane_u32(static_cast<uint32_t>(mine), own));
+                            }
+                        }
+                        run += tsum;
+                    }
+                    if (tok < 0) tok = last_pos;
+                    if (lane == 0) ss.bu[7] = static_cast<uint32_t>(tok);
                 }
-                if (tok < 0) tok = last_pos;
-                if (lane == 0) ss.bu[7] = static_cast<uint32_t>(tok);
+                __syncthreads();
+                token = ss.bu[7];
+                fast = true;
             }
-            __syncthreads();
-            token = ss.bu[7];
-            fast = true;
         }
     }
 

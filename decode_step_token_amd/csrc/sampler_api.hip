@@ -343,12 +343,12 @@ int sample_batch(dst_sampler* s, void* stream, const void* logits, int64_t row_s
             a.topk_idx_out = dbg->topk_idx_out;
             a.rand_out = dbg->rand_out;
         }
-        // batches of fewer rows than half the compute units spread each row
-        // over many workgroups; larger ones give each row a workgroup
-        const bool small = s->cus > 0 ? 2 * B < s->cus : B < 128;
+        // every sampled batch takes the one-workgroup-per-row kernel: measured
+        // on B = 1 .. 127 rows of 1024 to 151936 entries it is faster than the
+        // split-row kernel (which the entry point without allocations uses)
         if (flags & SAMPLER_DEBUG_FORCE_EXACT) {
             e = dst::launch_sample_exact(a, s->dtype, st);
-        } else if (split_ok && ((flags & SAMPLER_DEBUG_FORCE_SPLIT) || (!(flags & SAMPLER_DEBUG_FORCE_STREAM) && small))) {
+        } else if (split_ok && (flags & SAMPLER_DEBUG_FORCE_SPLIT)) {
             a.rec = s->rec;
             a.cand = s->cand;
             a.hist = s->hist;

@@ -76,10 +76,10 @@ enum sampler_status {
 /* sampler_debug.flags: run every row through the exact multi-pass path
  * (re-reads each row several times) instead of the single-pass kernel. */
 #define SAMPLER_DEBUG_FORCE_EXACT 1u
-/* ... through the one-workgroup-per-row kernel (batches of at least half as
- * many rows as compute units take it by default). */
+/* ... through the one-workgroup-per-row kernel (every batch with a
+ * temperature array takes it by default). */
 #define SAMPLER_DEBUG_FORCE_STREAM 2u
-/* ... through the split-row kernel (smaller batches take it by default; a
+/* ... through the split-row kernel, the one sample_batch_static runs (a
  * misaligned logits pointer or row stride falls back to the per-row kernel). */
 #define SAMPLER_DEBUG_FORCE_SPLIT 4u
 
