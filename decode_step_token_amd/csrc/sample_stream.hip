@@ -55,6 +55,12 @@ constexpr int kList = 64;
 constexpr int kTopKCands = 4096;          // top-k rows: candidate count the threshold aims below
 constexpr int kTopPTarget = 900;           // aimed-at candidate count for top-p rows
 constexpr int kBins = 1024;                // candidate histograms: 16 bins per lane of wave 0
+// Rows whose candidates are few (top-p, min_p, top-k up to kStageMaxK) keep
+// a lane's whole 16-byte load when it holds a candidate, two region slots
+// per load at the top of the wave's region, and expand the loads into
+// entries once, after the wave's stream.
+constexpr int kStageCap = kRegion / 2;     // staged loads per wave
+constexpr int kStageMaxK = 128;
 constexpr int kBinsPerLane = kBins / kWave;
 constexpr int kTilesPerLane = kMaxTiles / kWave;
 static_assert(kBins == kBlock, "one bin cleared per thread");
@@ -92,7 +98,7 @@ struct BlockPick {
 };
 
 struct Smem {
-    uint2 cent[kCap + kBlock];    // candidates: (value bits, later the order key; token index);
+    alignas(16) uint2 cent[kCap + kBlock];  // candidates: (value bits, later the order key; token index);
                                   // the last kBlock entries: one discard slot per thread
     float cw[kCap];
     float tref[kMaxTiles];
@@ -584,6 +590,16 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     float theta = INFINITY;
     const float c32 = static_cast<float>(c);
     uint32_t cnt = 0;                 // this wave's region fill (wave-uniform)
+    // Staged loads (wave-uniform count): load j of wave w in region slots
+    // w*kRegion + kRegion - 2(j+1) and +1, the index of its first element in
+    // cw[w*kRegion + j] (cw is unused until the stream ends).
+    const bool stage = want_cand && (mode == kTopP || prm.k <= kStageMaxK);
+    uint32_t nv = 0;
+    bool stage_ovf = false;
+    uint32_t* const stage_meta = reinterpret_cast<uint32_t*>(ss.cw) + wid * kRegion;
+    auto stage_vec = [&](uint32_t j) -> uint4* {
+        return reinterpret_cast<uint4*>(&ss.cent[wid * kRegion + kRegion - 2 * static_cast<int>(j) - 2]);
+    };
 
     float lref = -INFINITY;           // top-p rows: this lane's running reference
     double lsum = 0.0;                // ... and its exponent sum relative to it
@@ -600,9 +616,17 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     float m0 = -INFINITY;
 
     auto process = [&](const uint4* raw, int t) {
-        float tmax = IO::get(raw, 0);
+        // the maximum of each 16-byte load, then of the tile
+        float lm[IO::U];
 #pragma unroll
-        for (int q = 1; q < Q; ++q) tmax = fmaxf(tmax, IO::get(raw, q));
+        for (int uu = 0; uu < IO::U; ++uu) {
+            lm[uu] = IO::get(raw, uu * IO::VEC);
+#pragma unroll
+            for (int e = 1; e < IO::VEC; ++e) lm[uu] = fmaxf(lm[uu], IO::get(raw, uu * IO::VEC + e));
+        }
+        float tmax = lm[0];
+#pragma unroll
+        for (int uu = 1; uu < IO::U; ++uu) tmax = fmaxf(tmax, lm[uu]);
         if (tmax > best_x) {
             // the position inside the tile only matters to argmax rows
             if (mode == kArgmax) {
@@ -650,7 +674,23 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             for (int q = 0; q < Q; ++q) s += __builtin_amdgcn_exp2f(fmaf(IO::get(raw, q), c32, -lrc));
             lsum += static_cast<double>(s);
         }
-        if (want_cand && __ballot(tmax >= theta) != 0) {
+        if (stage && __ballot(tmax >= theta) != 0) {
+            // a lane's load that holds a value >= theta is kept whole, in
+            // (load, lane) order, which is token order
+            const uint32_t vbase = IO::index(t, lane, 0);
+#pragma unroll
+            for (int uu = 0; uu < IO::U; ++uu) {
+                const bool has = lm[uu] >= theta;
+                const uint64_t bm = __ballot(has);
+                if (bm == 0ull) continue;
+                const uint32_t j = nv + lane_rank(bm);
+                if (has && j < static_cast<uint32_t>(kStageCap)) {
+                    *stage_vec(j) = raw[uu];
+                    stage_meta[j] = vbase + static_cast<uint32_t>(uu * kWave * IO::VEC);
+                }
+                nv += static_cast<uint32_t>(__popcll(bm));
+            }
+        } else if (want_cand && __ballot(tmax >= theta) != 0) {
             // Slots in token order: the tile's index order is (load u, lane,
             // element), so each load needs its own prefix over the lanes.  The
             // per-load counts travel packed in one DPP scan (8-bit fields for
@@ -854,6 +894,71 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         best_q = -1;
     }
 
+    if (stage && !use_row) {
+        // Expand the staged loads into entries: every value >= theta as
+        // (value bits, index), in staging order (tiles in the order the wave
+        // read them, token order inside a tile), with each tile's first slot
+        // and count.  The loads are counted first, so that entries written
+        // from the region's start never reach staged loads (at its end) that
+        // are still to be read; a wave whose entries and staged loads would
+        // not both fit marks the row as overflowing.
+        constexpr int kTS = __builtin_ctz(IO::TILE);
+        const int rbase = wid * kRegion;
+        const uint32_t N = nv;
+        bool ovf = N > static_cast<uint32_t>(kStageCap);
+        uint32_t total = 0;
+        if (!ovf) {
+            for (uint32_t j0 = 0; j0 < N; j0 += kWave) {
+                const uint32_t j = j0 + static_cast<uint32_t>(lane);
+                uint32_t ce = 0;
+                if (j < N) {
+                    const uint4 v = *stage_vec(j);
+#pragma unroll
+                    for (int e = 0; e < IO::VEC; ++e) ce += IO::get(&v, e) >= theta ? 1u : 0u;
+                }
+                total += readlane_u32(wave_scan_u32_dpp(ce), kWave - 1);
+            }
+            ovf = total + 2u * N > static_cast<uint32_t>(kRegion);
+        }
+        if (ovf) {
+            stage_ovf = true;
+            cnt = 0;
+        } else {
+            uint32_t pos0 = 0;
+            for (uint32_t j0 = 0; j0 < N; j0 += kWave) {
+                const uint32_t j = j0 + static_cast<uint32_t>(lane);
+                const bool in = j < N;
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                uint32_t meta = 0, ce = 0;
+                if (in) {
+                    v = *stage_vec(j);
+                    meta = stage_meta[j];
+#pragma unroll
+                    for (int e = 0; e < IO::VEC; ++e) ce += IO::get(&v, e) >= theta ? 1u : 0u;
+                }
+                const uint32_t incl = wave_scan_u32_dpp(ce);
+                const uint32_t pstart = pos0 + incl - ce;
+                const uint32_t tl = meta >> kTS;
+                const bool first = in && (j == 0u || (stage_meta[j - 1] >> kTS) != tl);
+                const bool last = in && (j + 1u == N || (stage_meta[j + 1] >> kTS) != tl);
+                uint32_t pw = pstart;
+#pragma unroll
+                for (int e = 0; e < IO::VEC; ++e) {
+                    const float x = IO::get(&v, e);
+                    if (in && x >= theta) {
+                        ss.cent[rbase + static_cast<int>(pw)] = make_uint2(__float_as_uint(x), meta + static_cast<uint32_t>(e));
+                        ++pw;
+                    }
+                }
+                if (first) ss.tstart[tl] = static_cast<uint16_t>(rbase + static_cast<int>(pstart));
+                wave_lds_sync();
+                if (last) ss.tcnt[tl] = static_cast<uint16_t>(rbase + static_cast<int>(pw) - static_cast<int>(ss.tstart[tl]));
+                pos0 += readlane_u32(incl, kWave - 1);
+            }
+            cnt = pos0;
+        }
+    }
+
     // ------------------------------- this wave's share of the candidate tail --
     // top-p: the lane sums relative to m0; every candidate row: order keys and
     // the count histogram of this wave's region, top-p rows also weights
@@ -895,7 +1000,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         if (lane == 0) {
             atomicMax(reinterpret_cast<unsigned long long*>(&ss.mbest), static_cast<unsigned long long>(pk));
             atomicAdd(&ss.mtotal, cnt < static_cast<uint32_t>(kRegion) ? cnt : static_cast<uint32_t>(kRegion));
-            if (cnt > static_cast<uint32_t>(kRegion)) atomicOr(&ss.movf, 1u);
+            if (cnt > static_cast<uint32_t>(kRegion) || stage_ovf) atomicOr(&ss.movf, 1u);
         }
     }
     __syncthreads();
