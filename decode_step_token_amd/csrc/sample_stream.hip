@@ -61,6 +61,19 @@ constexpr int kBins = 1024;                // candidate histograms: 16 bins per 
 // entries once, after the wave's stream.
 constexpr int kStageCap = kRegion / 2;     // staged loads per wave
 constexpr int kStageMaxK = 128;
+// Flat top-p rows (the nucleus reaches far below the candidate threshold):
+// a weight histogram of 1024 bins, 16 per octave of the weight from 2^-64 up
+// (bin = the weight's fp32 exponent and top four mantissa bits), kept in
+// kHistCopies interleaved copies (lane l adds to copy l mod kHistCopies) in
+// the candidate regions.
+constexpr int kWBinBase = (127 - 64) << 4;
+constexpr int kHistCopies = 8;
+// A top-p row is taken for flat when the first tiles' weight at or above the
+// candidate threshold is below this fraction of p times their total weight;
+// the estimate is made only when the threshold lies within 2^kFlatGap (in
+// weight) of the first tiles' maximum, below which it cannot hold.
+constexpr double kFlatFrac = 0.5;
+constexpr float kFlatGap = 6.0f;
 constexpr int kBinsPerLane = kBins / kWave;
 constexpr int kTilesPerLane = kMaxTiles / kWave;
 static_assert(kBins == kBlock, "one bin cleared per thread");
@@ -140,6 +153,7 @@ struct Smem {
     uint32_t xidx[kList];
     uint32_t cut_key, cut_last;
     uint32_t next_tile;    // the stream's next unclaimed tile
+    uint32_t flat_bad;     // a flat row's weight reference had to be raised
 };
 
 // ------------------------------------------------------------ tile I/O --
@@ -614,6 +628,19 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     bool pre = false;
     uint32_t pre_lo = 0, pre_sh = 0;
     float m0 = -INFINITY;
+    // Flat top-p rows build the weight histogram while they stream (relative
+    // to m0, the weights the lane sums add), and collect no candidates.
+    // (bf16 rows only: the fp32 kernel has no registers to spare for it)
+    constexpr bool kFlatStream = DT == kDtypeBF16;
+    bool flatp = false;               // block-uniform
+    bool flat_bad = false;            // this lane raised its reference
+    double* const fhist = reinterpret_cast<double*>(ss.cent);
+    double* const fhl = fhist + (lane & (kHistCopies - 1));
+    static_assert(sizeof(double) * kBins * kHistCopies <= sizeof(ss.cent), "histogram copies fit");
+    auto wbin = [](float w) -> int {
+        const int q = static_cast<int>(__float_as_uint(w) >> 19) - kWBinBase;
+        return q < 0 ? 0 : (q > kBins - 1 ? kBins - 1 : q);
+    };
 
     auto process = [&](const uint4* raw, int t) {
         // the maximum of each 16-byte load, then of the tile
@@ -660,6 +687,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             // (a lane whose values so far are all padding (-inf) has no
             // reference yet; its lrc of +inf makes them add exactly 0)
             if (tmax > lref && (tmax - lref) * c32 > 30.0f) {
+                if constexpr (kFlatStream) flat_bad = true;
                 const float nrc = tmax * c32;
                 const float nrd = fmaf(tmax, c32, -nrc);
                 if (lsum > 0.0)
@@ -670,8 +698,18 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 lrd = nrd;
             }
             float s = 0.0f;
+            if (kFlatStream && flatp) {
 #pragma unroll
-            for (int q = 0; q < Q; ++q) s += __builtin_amdgcn_exp2f(fmaf(IO::get(raw, q), c32, -lrc));
+                for (int q = 0; q < Q; ++q) {
+                    // past the row's end the value is -inf: weight 0, bin 0
+                    const float w = __builtin_amdgcn_exp2f(fmaf(IO::get(raw, q), c32, -lrc));
+                    s += w;
+                    atomicAdd(&fhl[wbin(w) * kHistCopies], static_cast<double>(w));
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < Q; ++q) s += __builtin_amdgcn_exp2f(fmaf(IO::get(raw, q), c32, -lrc));
+            }
             lsum += static_cast<double>(s);
         }
         if (stage && __ballot(tmax >= theta) != 0) {
@@ -756,6 +794,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         ss.movf = 0u;
         ss.list_n = 0u;
         ss.next_tile = 2 * kWaves;
+        ss.flat_bad = 0u;
     }
     if (want_cand) {
         if (threadIdx.x < kMaxTiles) {
@@ -850,6 +889,41 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             lref = m0;
             lrc = m0 * c32;
             lrd = fmaf(m0, c32, -lrc);
+            if (kFlatStream && mode == kTopP && !(prm.min_p > 0.0f) && aligned && (m0 - theta) * c32 <= kFlatGap) {
+                // Is the row flat?  The first tiles' weight at or above theta
+                // against their total (weights relative to m0, all <= 1).
+                float zt = 0.0f, st = 0.0f;
+                if (t < n_tiles) {
+#pragma unroll
+                    for (int q = 0; q < Q; ++q) {
+                        const float x = IO::get(raw, q);
+                        const float w = __builtin_amdgcn_exp2f(fmaf(x, c32, -lrc));
+                        zt += w;
+                        st += x >= theta ? w : 0.0f;
+                    }
+                }
+                const double zw = wave_sum_dpp(static_cast<double>(zt));
+                const double sw = wave_sum_dpp(static_cast<double>(st));
+                if (lane == 0) {
+                    ss.tsum[wid] = zw;
+                    ss.tsum[kWaves + wid] = sw;
+                }
+                lds_barrier();
+                double z1 = 0.0, s1 = 0.0;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    z1 += ss.tsum[w];
+                    s1 += ss.tsum[kWaves + w];
+                }
+                if (s1 < kFlatFrac * static_cast<double>(prm.p) * z1) {
+                    flatp = true;
+                    pre = false;
+                    theta = INFINITY;          // no candidates
+#pragma unroll
+                    for (int cc = 0; cc < kHistCopies; ++cc) fhist[threadIdx.x * kHistCopies + cc] = 0.0;
+                    lds_barrier();
+                }
+            }
         } else {
             theta = -INFINITY;
         }
@@ -964,7 +1038,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     // the count histogram of this wave's region, top-p rows also weights
     // relative to m0 and the mass histogram
     const double m0c = static_cast<double>(m0) * c;
-    if (want_lanez && pre) {
+    if (want_lanez && (pre || flatp)) {
         const double part = lsum > 0.0
             ? lsum * exp2_neg((static_cast<double>(lref) - static_cast<double>(m0)) * c - static_cast<double>(lrd)) : 0.0;
         const double ws = wave_sum_dpp(part);
@@ -1002,6 +1076,9 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             atomicAdd(&ss.mtotal, cnt < static_cast<uint32_t>(kRegion) ? cnt : static_cast<uint32_t>(kRegion));
             if (cnt > static_cast<uint32_t>(kRegion) || stage_ovf) atomicOr(&ss.movf, 1u);
         }
+        if constexpr (kFlatStream) {
+            if (flatp && __ballot(flat_bad) != 0ull && lane == 0) atomicOr(&ss.flat_bad, 1u);
+        }
     }
     __syncthreads();
     const uint64_t best = ss.mbest;
@@ -1011,8 +1088,11 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     const uint32_t amax = 0xffffffffu - static_cast<uint32_t>(best);
     // top-p rows keep m0 as the weight reference while every weight relative
     // to it stays far below the float range; otherwise the row maximum
-    const bool pre_ok = pre && (mode != kTopP ||
-                                (static_cast<double>(m) - static_cast<double>(m0)) * c <= 64.0);
+    const bool pre_ok = (pre || flatp) && (mode != kTopP ||
+                                          (static_cast<double>(m) - static_cast<double>(m0)) * c <= 64.0);
+    // a flat row's histogram is complete unless some lane had to raise its
+    // reference (weights relative to m0 no longer fit)
+    const bool flat_ok = flatp && pre_ok && ss.flat_bad == 0u;
     const double mc = mode == kTopP && pre_ok ? m0c : static_cast<double>(m) * c;
     // min_p keeps p_i >= min_p * p_max, that is x >= m + T ln(min_p): the
     // threshold in fp64, as the order key of the smallest float at or above
@@ -1437,7 +1517,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
     //   top-p: the same descent by weight, inside the top-k cut;
     //   the draw: per-tile kept weight, a scan over the tiles, then a scan of
     //     the one tile's entries in slot order, which is token order.
-    if (want_cand) {
+    if (want_cand && !flatp) {
         if (overflow || (mode == kTopK && n_total < static_cast<uint32_t>(prm.k))) {
             use_row = true;
         } else {
@@ -2090,24 +2170,19 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         // heavier); lighter weights and zero fall into bin 0, weights from
         // about 0.97 up into the top bin.  Bin edges are bit patterns of the
         // weight, so the second pass classifies a value with integer compares.
-        constexpr int kWBinBase = (127 - 64) << 4;
-        auto wbin = [&](float w) -> int {
-            const int q = static_cast<int>(__float_as_uint(w) >> 19) - kWBinBase;
-            return q < 0 ? 0 : (q > kBins - 1 ? kBins - 1 : q);
-        };
         // pass A's histogram: kHistCopies adjacent copies of each bin, lane l
         // adding to copy l mod kHistCopies (so lanes of a wave seldom meet on one
         // address), kept in the candidate regions, which pass B refills (fp64:
         // LDS fp32 atomic adds run an order of magnitude slower here)
-        constexpr int kHistCopies = 8;
-        static_assert(sizeof(double) * kBins * kHistCopies <= sizeof(ss.cent), "histogram copies fit");
-        double* const hist = reinterpret_cast<double*>(ss.cent);
+        double* const hist = fhist;
+        if (!flat_ok) {
 #pragma unroll
-        for (int c = 0; c < kHistCopies; ++c) hist[threadIdx.x * kHistCopies + c] = 0.0;
+            for (int c = 0; c < kHistCopies; ++c) hist[threadIdx.x * kHistCopies + c] = 0.0;
+        }
         if (threadIdx.x == 0) { ss.movf = 0u; ss.mtotal = 0u; }
         __syncthreads();
-        // (A)
-        {
+        // (A), unless the stream built the histogram
+        if (!flat_ok) {
             double* const hl = hist + (lane & (kHistCopies - 1));
             uint4 ra[IO::U], rb[IO::U];
             int tt = wid;
