@@ -2,8 +2,8 @@
 //
 // "The scheduler skeleton and the offline interface", section "Preparing a
 // batch": _make_write_tuple gives each request (row = table_idx, col =
-// device_len), or col = -1 for a request that must not be written, which
-// lands harmlessly in the last column; section "_forward": the sampled
+// device_len), or col = -1 for a request whose token is not to be kept; -1
+// indexes the pool's last column, a cell no request reads; section "_forward": the sampled
 // tokens are scattered into token_pool[rows, cols] on the device, so the
 // CPU never needs the token values.
 //

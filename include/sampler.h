@@ -144,7 +144,8 @@ DST_API int sampler_destroy(dst_sampler* s);
  *   top_p       dev [B] fp32 or NULL (disabled).  Clamped to [1e-6, 1];
  *               1 disables.  top-k is applied first, then top-p on the
  *               renormalised survivors; a rank is kept while the mass before
- *               it is < top_p, so the most likely token is always kept.
+ *               it is < top_p (the top rank, with nothing before it, is
+ *               never cut).
  *   min_p       dev [B] fp32 or NULL (disabled); the pages' exercise
  *               ("The engine and the sampler", section "Exercises"): keep
  *               the tokens whose probability (temperature applied, full

@@ -14,7 +14,7 @@ It follows the mini-sglang pages step by step, in float64:
   logits / T, sort descending, top-k mask by rank, renormalise, mask the
   ranks whose preceding mass is already >= top_p, scatter back to index
   order, one categorical draw).  The same section states the order: top-k
-  first, then top-p, and that the most likely token is always kept.
+  first, then top-p; the top rank has an empty prefix, so it survives every cut.
 * "The engine and the sampler", section "forward_batch": tokens are int32;
   one copy stays on the device, one goes to the host.
 * "The scheduler skeleton and the offline interface", section "Preparing a

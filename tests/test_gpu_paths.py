@@ -76,6 +76,24 @@ def test_flat_bf16_rows_with_ties(path):
 
 
 @pytest.mark.parametrize("path", ["stream", "split"])
+def test_flat_bf16_rows_late_spike(path):
+    """bf16 rows at T = 1.5 that the first tiles show to be flat, so the
+    per-row kernel builds their weight histogram while it streams.  A value
+    beyond the first tiles by far more than 2^30 in weight makes that row
+    build the histogram again after the stream (the nucleus is then that one
+    token); a value 3 above the maximum lands in the top bin; the other rows
+    are plain flat rows."""
+    rng = np.random.default_rng(23)
+    w = wl.tiny(rng, 24, 152064, "bf16", scale=2.5)
+    x = wl.bf16_bits_to_f32(w.logits)
+    for b in range(w.B):
+        j = int(rng.integers(60000, w.V))
+        x[b, j] = x[b].max() + (40.0, 3.0, 0.0)[b % 3]
+    w.logits = wl.to_bf16_bits(x)
+    _check(_flat(w, p=(0.9, 0.95)), path, probs_rows={0, 1, 2, 23})
+
+
+@pytest.mark.parametrize("path", ["stream", "split"])
 def test_min_p_mix(path):
     w = wl.with_min_p(wl.tiny(np.random.default_rng(22), 48, 40000, "f32"),
                       [0.0, 0.01, 0.05, 0.2, 0.5], 22)

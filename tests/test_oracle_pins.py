@@ -205,7 +205,7 @@ def test_bf16_rows_widen_exactly():
     ((0.5, 0.25, 0.125, 0.125), 4, 0.75, 2),
     ((0.5, 0.25, 0.125, 0.125), 4, 0.75 + 2 ** -20, 3),
     ((0.5, 0.25, 0.125, 0.125), 4, 0.5, 1),
-    ((0.5, 0.25, 0.125, 0.125), 4, 2 ** -30, 1),        # the most likely token is always kept
+    ((0.5, 0.25, 0.125, 0.125), 4, 2 ** -30, 1),        # rank 0's prefix is empty: it survives any p
     ((0.5, 0.25, 0.125, 0.125), 4, 1.0, 4),
     # top-k 2 renormalises (1/2, 1/4) to (2/3, 1/3): prefix 2/3 >= 0.6 drops rank 1
     ((0.5, 0.25, 0.125, 0.125), 2, 0.6, 1),
