@@ -42,14 +42,29 @@ HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=unde
             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 
+# sources whose kernels must use no scratch memory: the per-row kernel fills
+# every VGPR of a CU, and a spill to scratch costs ~10 us per launch
+NO_SCRATCH = ("sample_stream.hip",)
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in p.stdout.splitlines()
-                    if "packed-fp32-ops" not in l and "warning generated" not in l)
     if p.returncode != 0:
         raise RuntimeError(f"command failed ({p.returncode}): {' '.join(cmd)}\n{p.stdout}")
+    if RESOURCE_REMARKS in cmd:
+        kernel = None
+        for line in p.stdout.splitlines():
+            if "Function Name:" in line:
+                kernel = line.split("Function Name:")[1].split()[0]
+            elif "ScratchSize [bytes/lane]:" in line:
+                n = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
+                if n:
+                    raise RuntimeError(f"{kernel} uses {n} bytes of scratch per lane: {' '.join(cmd)}")
+    out = "\n".join(l for l in p.stdout.splitlines()
+                    if "packed-fp32-ops" not in l and "warning generated" not in l and "remark:" not in l)
     if verbose and out.strip():
         print(out, flush=True)
 
@@ -66,7 +81,8 @@ def build(verbose: bool = False, jobs: int | None = None, host_check: bool = Tru
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *CFLAGS, *([RESOURCE_REMARKS] if src in NO_SCRATCH else []),
+                     "-c", os.path.join(CSRC, src), "-o", obj])
     if host_check:
         for src in SOURCES + ["host_check.cpp"]:
             obj = os.path.join(SAN_BUILD, os.path.splitext(src)[0] + ".o")

@@ -613,7 +613,7 @@ def test_cutoff_band_hand_worked():
     keeps exactly one of them.  The first prefix is exactly 0: at the
     clamped top_p = float32(1e-6) only the first token is kept, with no
     alternative ("The engine and the sampler", section "The sampler": the
-    most likely token always stays)."""
+    top rank, with nothing before it, survives every cut)."""
     q = np.array([0.5, 0.25, 0.125, 0.125])
     assert sr.cutoff_alternatives(q, 4, 0.75 - 5e-7) == {2, 3}
     assert sr.cutoff_alternatives(q, 4, 0.75 + 5e-7) == {2, 3}
