@@ -72,7 +72,7 @@ constexpr int kHistCopies = 8;
 // candidate threshold is below this fraction of p times their total weight;
 // the estimate is made only when the threshold lies within 2^kFlatGap (in
 // weight) of the first tiles' maximum, below which it cannot hold.
-constexpr double kFlatFrac = 0.5;
+constexpr double kFlatFrac = 0.8;
 constexpr float kFlatGap = 6.0f;
 constexpr int kBinsPerLane = kBins / kWave;
 constexpr int kTilesPerLane = kMaxTiles / kWave;
