@@ -169,6 +169,15 @@ struct TileIO {
     // Past the end of the row the values are -inf.
     __device__ static __forceinline__ void load(const void* row, int V, int t, int lane, uint4* raw) {
         const int64_t base = static_cast<int64_t>(t) * TILE;
+        if (base + TILE <= V) {
+            // a whole tile inside the row: no per-load bounds (the test is
+            // wave-uniform)
+            const char* p = static_cast<const char*>(row) + (base + lane * VEC) * (DT == kDtypeF32 ? 4 : 2);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                raw[u] = ld_global_u4_stream(p + u * kWave * VEC * (DT == kDtypeF32 ? 4 : 2));
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t off = base + u * kWave * VEC + lane * VEC;
@@ -514,7 +523,7 @@ __device__ __forceinline__ bool long_row(const SampleArgs& a, int r) {
     return !p.greedy && p.k == a.V && (p.top_p || p.min_p > 0.0f);
 }
 
-__device__ int long_rows_first(const SampleArgs& a, int g) {
+__device__ __forceinline__ int long_rows_first(const SampleArgs& a, int g) {
     const int lane = threadIdx.x & (kWave - 1);
     // one coalesced read per parameter and 64 rows (rows past B read row
     // B - 1 and are masked off), the long-row masks kept per 64 rows
