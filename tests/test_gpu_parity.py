@@ -107,6 +107,30 @@ def test_late_maximum_weight_reference():
     _check(w)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_clustered_candidates(dtype):
+    """Rows whose large values sit in one contiguous block past the first
+    tiles: every value of the block clears the threshold the first tiles
+    give, so the wave that reads those tiles collects far more candidates
+    than it can hold (staged loads for top-p and small top-k, per-element
+    entries for top-k above 128), and the row must still match the oracle
+    (it finishes from the row itself).  Rows with a smaller block stay within
+    the candidate regions."""
+    rng = np.random.default_rng(29)
+    B, V = 16, 151936
+    w = wl.tiny(rng, B, V, dtype)
+    x = w.logits.astype(np.float32) if dtype == "f32" else wl.bf16_bits_to_f32(w.logits)
+    for b in range(B):
+        n = (3000, 400, 100)[b % 3]
+        j0 = int(rng.integers(40000, V - n))
+        x[b, j0:j0 + n] = 7.0 + rng.standard_normal(n).astype(np.float32) * 0.5
+    w.logits = x if dtype == "f32" else wl.to_bf16_bits(x)
+    w.temperature[:] = np.float32(0.8)
+    w.top_k[:] = np.array([-1, 20, 64, 200, 1000, -1, 50, -1] * 2, dtype=np.int32)
+    w.top_p[:] = np.array([0.9, 1.0, 0.95, 1.0, 0.9, 0.5, 0.8, 0.99] * 2, dtype=np.float32)
+    _check(w, probs_rows={0, 1, 5})
+
+
 def test_greedy_batch_without_temperature_bf16():
     rng = np.random.default_rng(13)
     w = wl.tiny(rng, 100, 7000, "bf16")
