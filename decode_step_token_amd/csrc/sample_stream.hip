@@ -2235,14 +2235,9 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
         const uint32_t whi = dpick == kBins - 1 ? 0xffffffffu : static_cast<uint32_t>(dpick + 1 + kWBinBase) << 19;
         // (B)
         {
-            // the bin test of one value: its weight's bit pattern in [wlo, whi)
-            auto in_bin = [&](float x) {
-                const uint32_t wb = __float_as_uint(__builtin_amdgcn_exp2f(fmaf(x, c32, -Pf)));
-                return wb >= wlo && wb < whi;
-            };
             uint4 ra[IO::U], rb[IO::U];
-            uint32_t nabove = 0;
-            uint32_t nst = 0;                  // staged loads (wave-uniform)
+            uint32_t fill = 0, nabove = 0;
+            const uint32_t rbeg = static_cast<uint32_t>(wid * kRegion);
             int tt = wid;
             if (tt < n_tiles) IO::load(row, V, tt, lane, ra);
             for (; tt < n_tiles; tt += kWaves) {
@@ -2250,101 +2245,48 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
                 for (int v = 0; v < IO::U; ++v) rb[v] = ra[v];
                 if (tt + kWaves < n_tiles) IO::load(row, V, tt + kWaves, lane, ra);
                 // the lane's weights above the bin: at most Q of them, summed
-                // in fp32 (relative error below Q * 2^-24), then in fp64; a
-                // 16-byte load holding an entry inside the bin is staged whole
-                // (as the stream stages candidates) and expanded after the pass
+                // in fp32 (relative error below Q * 2^-24), then in fp64; its
+                // entries inside the bin as a bit mask, stored after one scan
+                // of the lanes' counts
                 float part = 0.0f;
+                float wq[Q];
+                uint32_t inm = 0u;
 #pragma unroll
-                for (int uu = 0; uu < IO::U; ++uu) {
-                    bool has = false;
+                for (int q = 0; q < Q; ++q) {
+                    const float w = __builtin_amdgcn_exp2f(fmaf(IO::get(rb, q), c32, -Pf));
+                    wq[q] = w;
+                    const uint32_t wb = __float_as_uint(w);
+                    const bool up = wb >= whi;
+                    part += up ? w : 0.0f;
+                    nabove += up ? 1u : 0u;
+                    inm |= (wb >= wlo && wb < whi ? 1u : 0u) << q;
+                }
+                const uint32_t ln = static_cast<uint32_t>(__popc(inm));
+                const uint32_t incl = wave_scan_u32_dpp(ln);
+                const uint32_t tot = readlane_u32(incl, kWave - 1);
+                if (tot != 0u) {
+                    uint32_t pos = fill + incl - ln;
 #pragma unroll
-                    for (int e = 0; e < IO::VEC; ++e) {
-                        const float w = __builtin_amdgcn_exp2f(fmaf(IO::get(rb, uu * IO::VEC + e), c32, -Pf));
-                        const uint32_t wb = __float_as_uint(w);
-                        const bool up = wb >= whi;
-                        part += up ? w : 0.0f;
-                        nabove += up ? 1u : 0u;
-                        has = has || (wb >= wlo && wb < whi);
-                    }
-                    const uint64_t bm = __ballot(has);
-                    if (bm != 0ull) {
-                        const uint32_t j = nst + lane_rank(bm);
-                        if (has && j < static_cast<uint32_t>(kStageCap)) {
-                            *stage_vec(j) = rb[uu];
-                            stage_meta[j] = IO::index(tt, lane, uu * IO::VEC);
+                    for (int q = 0; q < Q; ++q) {
+                        if ((inm >> q) & 1u) {
+                            if (pos < static_cast<uint32_t>(kRegion)) {
+                                ss.cent[rbeg + pos] = make_uint2(f32_key(IO::get(rb, q)), IO::index(tt, lane, q));
+                                ss.cw[rbeg + pos] = static_cast<float>(static_cast<double>(wq[q]) * G);
+                            }
+                            ++pos;
                         }
-                        nst += static_cast<uint32_t>(__popcll(bm));
                     }
+                    fill += tot;
                 }
                 const double ts = wave_sum_dpp(static_cast<double>(part));
                 if (lane == 0) ss.tacc[tt] = ts * G;
-            }
-            // Expand the staged loads into entries (order key, index) from the
-            // region's start, counting first so that no entry reaches a staged
-            // load still to be read; then the entries' weights (the staged
-            // loads' indices, kept in the weight array, are read by then).
-            const int rbase = wid * kRegion;
-            const uint32_t N = nst;
-            bool ovf = N > static_cast<uint32_t>(kStageCap);
-            uint32_t total = 0;
-            if (!ovf) {
-                for (uint32_t j0 = 0; j0 < N; j0 += kWave) {
-                    const uint32_t j = j0 + static_cast<uint32_t>(lane);
-                    uint32_t ce = 0;
-                    if (j < N) {
-                        const uint4 v = *stage_vec(j);
-                        const uint32_t meta = stage_meta[j];
-#pragma unroll
-                        for (int e = 0; e < IO::VEC; ++e)
-                            ce += meta + static_cast<uint32_t>(e) < static_cast<uint32_t>(V) && in_bin(IO::get(&v, e)) ? 1u : 0u;
-                    }
-                    total += readlane_u32(wave_scan_u32_dpp(ce), kWave - 1);
-                }
-                ovf = total + 2u * N > static_cast<uint32_t>(kRegion);
-            }
-            uint32_t fill = static_cast<uint32_t>(kRegion) + 1u;
-            if (!ovf) {
-                uint32_t pos0 = 0;
-                for (uint32_t j0 = 0; j0 < N; j0 += kWave) {
-                    const uint32_t j = j0 + static_cast<uint32_t>(lane);
-                    const bool in = j < N;
-                    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                    uint32_t meta = 0, ce = 0, msk = 0;
-                    if (in) {
-                        v = *stage_vec(j);
-                        meta = stage_meta[j];
-#pragma unroll
-                        for (int e = 0; e < IO::VEC; ++e) {
-                            const bool ib = meta + static_cast<uint32_t>(e) < static_cast<uint32_t>(V) && in_bin(IO::get(&v, e));
-                            msk |= (ib ? 1u : 0u) << e;
-                        }
-                        ce = static_cast<uint32_t>(__popc(msk));
-                    }
-                    const uint32_t incl = wave_scan_u32_dpp(ce);
-                    uint32_t pw = pos0 + incl - ce;
-#pragma unroll
-                    for (int e = 0; e < IO::VEC; ++e) {
-                        if ((msk >> e) & 1u) {
-                            ss.cent[rbase + static_cast<int>(pw)] = make_uint2(f32_key(IO::get(&v, e)), meta + static_cast<uint32_t>(e));
-                            ++pw;
-                        }
-                    }
-                    pos0 += readlane_u32(incl, kWave - 1);
-                }
-                fill = pos0;
-                wave_lds_sync();
-                for (uint32_t i = static_cast<uint32_t>(lane); i < fill; i += kWave) {
-                    const float x = key_f32(ss.cent[rbase + static_cast<int>(i)].x);
-                    const float w = __builtin_amdgcn_exp2f(fmaf(x, c32, -Pf));
-                    ss.cw[rbase + static_cast<int>(i)] = static_cast<float>(static_cast<double>(w) * G);
-                }
             }
             nabove = readlane_u32(wave_scan_u32_dpp(nabove), kWave - 1);
             if (lane == 0) {
                 if (fill > static_cast<uint32_t>(kRegion)) atomicOr(&ss.movf, 1u);
                 atomicAdd(&ss.mtotal, nabove);
             }
-            cnt = fill > static_cast<uint32_t>(kRegion) ? 0u : fill;
+            cnt = fill;
         }
         __syncthreads();
         if (ss.movf == 0u) {

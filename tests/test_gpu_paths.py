@@ -94,6 +94,25 @@ def test_flat_bf16_rows_late_spike(path):
 
 
 @pytest.mark.parametrize("path", ["stream", "split"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_flat_rows_crowded_boundary_bin(path, dtype):
+    """Top-p rows at T = 1.5 with a block of one repeated value (2,000 to
+    100,000 copies at random positions).  The larger blocks hold enough of the
+    mass for the nucleus to end inside them, so the boundary bin holds tens of
+    thousands of equal entries, cut in token order; that many entries do not
+    fit the per-wave regions, and the row is finished from the row itself.
+    The smaller blocks fit."""
+    rng = np.random.default_rng(31)
+    w = wl.tiny(rng, 16, 152064, dtype, scale=2.5)
+    x = wl.bf16_bits_to_f32(w.logits) if dtype == "bf16" else w.logits
+    for b in range(w.B):
+        n = (2000, 5000, 20000, 100000)[b % 4]
+        x[b, rng.choice(w.V, n, replace=False)] = 0.0
+    w.logits = wl.to_bf16_bits(x) if dtype == "bf16" else x
+    _check(_flat(w, p=(0.9, 0.95)), path, probs_rows={0, 3, 6, 15})
+
+
+@pytest.mark.parametrize("path", ["stream", "split"])
 def test_min_p_mix(path):
     w = wl.with_min_p(wl.tiny(np.random.default_rng(22), 48, 40000, "f32"),
                       [0.0, 0.01, 0.05, 0.2, 0.5], 22)
