@@ -131,6 +131,26 @@ def test_clustered_candidates(dtype):
     _check(w, probs_rows={0, 1, 5})
 
 
+@pytest.mark.parametrize("f_first", [0.5, 1.6])
+def test_unrepresentative_first_tiles(f_first):
+    """c2-like rows (bf16, N(0, 3), half greedy, T = 0.7 with top-p 0.9) whose
+    first 16,384 logits have another spread than the rest.  The threshold
+    comes from the first tiles, so it lands too low (narrower start: far more
+    candidates than the regions hold) or too high (wider start: nuclei reach
+    below it); either way the rows must still match the oracle."""
+    rng = np.random.default_rng(1002 + int(f_first * 10))
+    B, V = 32, 128256
+    x = rng.standard_normal((B, V), dtype=np.float32) * np.float32(3.0)
+    x[:, :16384] *= np.float32(f_first)
+    w = wl.tiny(rng, B, V, "bf16")
+    w.logits = wl.to_bf16_bits(x)
+    greedy = np.arange(B) % 2 == 0
+    w.temperature = np.where(greedy, 0.0, 0.7).astype(np.float32)
+    w.top_k = None
+    w.top_p = np.where(greedy, 1.0, 0.9).astype(np.float32)
+    _check(w, probs_rows={1, 3, 31})
+
+
 def test_greedy_batch_without_temperature_bf16():
     rng = np.random.default_rng(13)
     w = wl.tiny(rng, 100, 7000, "bf16")
