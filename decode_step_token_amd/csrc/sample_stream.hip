@@ -2188,7 +2188,7 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
 #pragma unroll
             for (int c = 0; c < kHistCopies; ++c) hist[threadIdx.x * kHistCopies + c] = 0.0;
         }
-        if (threadIdx.x == 0) { ss.movf = 0u; ss.mtotal = 0u; }
+        if (threadIdx.x == 0) { ss.movf = 0u; ss.mtotal = 0u; ss.next_tile = kWaves; }
         __syncthreads();
         // (A), unless the stream built the histogram
         if (!flat_ok) {
@@ -2238,12 +2238,19 @@ __global__ __launch_bounds__(kBlock) void sample_stream_kernel(SampleArgs a) {
             uint4 ra[IO::U], rb[IO::U];
             uint32_t fill = 0, nabove = 0;
             const uint32_t rbeg = static_cast<uint32_t>(wid * kRegion);
-            int tt = wid;
-            if (tt < n_tiles) IO::load(row, V, tt, lane, ra);
-            for (; tt < n_tiles; tt += kWaves) {
+            // a wave's first tile is its index; after that it claims the next
+            // unread tile as it starts on one, as in the stream, so that the
+            // waves finish close together
+            int tn = wid;
+            if (tn < n_tiles) IO::load(row, V, tn, lane, ra);
+            while (tn < n_tiles) {
+                const int tt = tn;
 #pragma unroll
                 for (int v = 0; v < IO::U; ++v) rb[v] = ra[v];
-                if (tt + kWaves < n_tiles) IO::load(row, V, tt + kWaves, lane, ra);
+                uint32_t cl = 0;
+                if (lane == 0) cl = atomicAdd(&ss.next_tile, 1u);
+                tn = __builtin_amdgcn_readfirstlane(static_cast<int>(cl));
+                if (tn < n_tiles) IO::load(row, V, tn, lane, ra);
                 // the lane's weights above the bin: at most Q of them, summed
                 // in fp32 (relative error below Q * 2^-24), then in fp64; its
                 // entries inside the bin as a bit mask, stored after one scan
